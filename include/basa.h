@@ -1,0 +1,103 @@
+/*
+ * basa.h: C ABI of the MI355X (gfx950) shifted local-window attention library.
+ *
+ * Source of the operation: "Backend-Agnostic Sparse Attention for Fast High-Resolution
+ * Visual Generation" (Ma, Song, Wu, Liu, Zhao; arXiv 2610.08772).
+ *   §3.1 "Shifted Window Sparse Attention": the visual token grid is cyclically shifted
+ *        by -Delta, partitioned into non-overlapping windows, each window gets standard
+ *        scaled dot-product softmax attention, and the outputs are shifted back by +Delta.
+ *   App. A.1 "Regular execution with standard attention backends": the partition applies
+ *        to grids exactly divisible by the window; windows are independent dense
+ *        attention problems.
+ *   Fig. 3(b): the operation replaces a DiT's visual self-attention; its inputs are the
+ *        already-projected (and position-encoded) q, k, v, its output is the attention
+ *        output before the output projection.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are contiguous [B, heads, N, head_dim], N = T*H*W tokens flattened
+ *     row-major over (t, h, w). q, k, v, out hold the same element type.
+ *   - All tensor pointers are DEVICE pointers owned by the caller and must be 16-byte
+ *     aligned. The library allocates nothing and keeps no state between calls.
+ *   - Calls are asynchronous on `stream` (0 = the null stream) and return once the work
+ *     is enqueued. Argument errors are reported before any HIP call is made; no entry
+ *     point aborts, throws or prints.
+ *   - The softmax scale is 1/sqrt(head_dim); softmax statistics are kept in fp32.
+ *   - Supported: dtype BASA_DTYPE_F32 or BASA_DTYPE_BF16, head_dim 64 or 128.
+ */
+#ifndef BASA_H
+#define BASA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BASA_DTYPE_F32 = 0,  /* IEEE binary32 */
+  BASA_DTYPE_BF16 = 1  /* bfloat16, fp32 accumulation, output rounded to nearest even */
+} basa_dtype;
+
+typedef enum {
+  BASA_OK = 0,
+  BASA_ERR_NULL = 1,        /* a required pointer is NULL */
+  BASA_ERR_SHAPE = 2,       /* non-positive size, or window does not divide the grid */
+  BASA_ERR_UNSUPPORTED = 3, /* dtype or head_dim outside the supported set */
+  BASA_ERR_ALIAS = 4,       /* out overlaps q, k or v */
+  BASA_ERR_OVERFLOW = 5,    /* a size or index does not fit the 32-bit per-head indexing */
+  BASA_ERR_HIP = 6,         /* the HIP runtime rejected the launch (hipGetLastError) */
+  BASA_ERR_ALIGN = 7        /* a tensor pointer is not 16-byte aligned */
+} basa_status;
+
+/*
+ * Shifted local-window attention (paper §3.1).
+ *
+ * Grid (T, H, W) and window (wt, wh, ww): every window size must be positive and divide
+ * its grid size exactly (App. A.1); otherwise BASA_ERR_SHAPE. Images use T = wt = 1; the
+ * paper's video windows span the whole temporal axis (wt = T), smaller wt is allowed.
+ * Shift (st, sh, sw): any integers, reduced modulo (T, H, W). Along each axis, window m
+ * local slot l reads and writes the original position (m*w + l + shift) mod n, i.e. the
+ * grid is rolled by -shift before partitioning and the output rolled back by +shift.
+ * Windows that wrap around the grid edge attend across it; there is no mask.
+ *
+ * out[b, h, i, :] = sum_{j in win(i)} softmax_j(q_i . k_j / sqrt(head_dim)) v_j.
+ *
+ * out must not overlap q, k or v (BASA_ERR_ALIAS). Returns a basa_status.
+ */
+int basa_window_attn_fwd(const void* q, const void* k, const void* v, void* out,
+                         int B, int heads, int T, int H, int W,
+                         int wt, int wh, int ww, int st, int sh, int sw,
+                         int head_dim, int dtype, hipStream_t stream);
+
+/*
+ * Dense softmax attention over all N tokens: the baseline the paper's speedups are
+ * measured against (§4, Tables 2 and 3, "Dense" rows). It runs the same kernel as
+ * basa_window_attn_fwd with grid (1, 1, N), window (1, 1, N) and no shift.
+ * Same conventions and errors as basa_window_attn_fwd.
+ */
+int basa_full_attn_fwd(const void* q, const void* k, const void* v, void* out,
+                       int B, int heads, int N, int head_dim, int dtype, hipStream_t stream);
+
+/*
+ * Window membership export (paper §3.1): perm[m * Wtok + l] = flat original token of
+ * local slot l of window m, Wtok = wt*wh*ww, windows numbered row-major over window
+ * coordinates (t, h, w) and slots row-major over local coordinates (t, h, w). The table
+ * is written on the device by the same index function the attention kernels use.
+ * perm: device pointer to T*H*W int32 (4-byte aligned). Same shape and shift rules and
+ * errors as basa_window_attn_fwd.
+ */
+int basa_window_perm(int T, int H, int W, int wt, int wh, int ww, int st, int sh, int sw,
+                     int32_t* perm, hipStream_t stream);
+
+/* Static, NUL-terminated description of a basa_status value. Never NULL. */
+const char* basa_status_string(int status);
+
+/* Library ABI version: (major << 16) | minor. */
+int basa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BASA_H */

@@ -7,6 +7,7 @@ from .basa_oracle import (  # noqa: F401
     check_partition,
     full_attention,
     full_attention_rows,
+    members_of,
     reduce_shift,
     window_attention,
     window_attention_loops,

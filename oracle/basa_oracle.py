@@ -94,6 +94,24 @@ def window_members(grid: Sequence[int], window: Sequence[int], shift: Sequence[i
     return table
 
 
+def members_of(grid: Sequence[int], window: Sequence[int], shift: Sequence[int], token: int) -> np.ndarray:
+    """Members (flat original tokens, in local order) of the window holding ``token``:
+    the rolled position of the token along each axis is (p - s) mod n, its window
+    coordinate that position // w; the members then follow the same rule as
+    ``window_members``. Lets huge grids be sampled without building the whole table."""
+    (T, H, W), (wt, wh, ww) = check_partition(grid, window)
+    st, sh, sw = reduce_shift(grid, shift)
+    token = int(token)
+    pt, ph, pw = token // (H * W), (token // W) % H, token % W
+    mt, mh, mw = ((pt - st) % T) // wt, ((ph - sh) % H) // wh, ((pw - sw) % W) // ww
+    out = []
+    for lt in range(wt):
+        for lh in range(wh):
+            for lw in range(ww):
+                out.append((((mt * wt + lt + st) % T) * H + (mh * wh + lh + sh) % H) * W + (mw * ww + lw + sw) % W)
+    return np.array(out, dtype=np.int64)
+
+
 def _attend(Qw: np.ndarray, Kw: np.ndarray, Vw: np.ndarray, scale: float):
     """Dense softmax(Q K^T * scale) V for one window, plus the per-row log-sum-exp of
     the scaled logits. Plain definition, with the usual max subtraction."""
@@ -106,13 +124,20 @@ def _attend(Qw: np.ndarray, Kw: np.ndarray, Vw: np.ndarray, scale: float):
     return O, lse
 
 
-def _check_qkv(q, k, v):
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
+def _check_qkv(q, k, v, upcast=True):
+    """Shape check; with ``upcast`` the arrays are converted to float64 as a whole. The
+    sampled-row functions pass upcast=False and convert each gathered slice instead, so
+    full-size float32 inputs are never copied in full (the arithmetic is float64 either
+    way)."""
+    if upcast:
+        q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
         raise ValueError(f"q, k, v must share one [B, heads, N, d] shape: {q.shape} {k.shape} {v.shape}")
     return q, k, v
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
 
 
 def window_attention(q, k, v, grid, window, shift, *, return_lse: bool = False):
@@ -189,7 +214,7 @@ def window_attention_rows(q, k, v, grid, window, shift, rows):
     """Output rows ``rows`` (flat original token indices) of window attention, for all
     (batch, head); shape [B, heads, len(rows), d]. Each row is computed on its own from
     its window's keys and values, so full-size workloads can be sampled cheaply."""
-    q, k, v = _check_qkv(q, k, v)
+    q, k, v = _check_qkv(q, k, v, upcast=False)
     B, Hh, N, d = q.shape
     table = window_members(grid, window, shift)
     owner = np.empty(N, dtype=np.int64)
@@ -202,7 +227,7 @@ def window_attention_rows(q, k, v, grid, window, shift, rows):
         for h in range(Hh):
             for r_i, r in enumerate(rows):
                 members = table[owner[r]]
-                O, _ = _attend(q[b, h, r:r + 1], k[b, h, members], v[b, h, members], scale)
+                O, _ = _attend(_f64(q[b, h, r:r + 1]), _f64(k[b, h, members]), _f64(v[b, h, members]), scale)
                 out[b, h, r_i] = O[0]
     return out
 
@@ -223,12 +248,12 @@ def full_attention(q, k, v, *, return_lse: bool = False):
 
 def full_attention_rows(q, k, v, rows):
     """Rows ``rows`` of dense attention, [B, heads, len(rows), d]."""
-    q, k, v = _check_qkv(q, k, v)
+    q, k, v = _check_qkv(q, k, v, upcast=False)
     B, Hh, N, d = q.shape
     rows = np.asarray(rows, dtype=np.int64)
     scale = 1.0 / math.sqrt(d)
     out = np.empty((B, Hh, rows.size, d), dtype=np.float64)
     for b in range(B):
         for h in range(Hh):
-            out[b, h], _ = _attend(q[b, h, rows], k[b, h], v[b, h], scale)
+            out[b, h], _ = _attend(_f64(q[b, h, rows]), _f64(k[b, h]), _f64(v[b, h]), scale)
     return out

@@ -1,0 +1,130 @@
+"""ctypes binding of ``libbasa.so`` (declarations and contracts: include/basa.h).
+
+Argument marshalling only: torch tensors supply device pointers and the current HIP
+stream, every computation runs in the library's kernels. There is no fallback: if the
+library is missing or a call fails, a ``BasaError`` is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbasa.so")
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+# Exported C symbols, in header order.
+SYMBOLS = ("basa_window_attn_fwd", "basa_full_attn_fwd", "basa_window_perm",
+           "basa_status_string", "basa_version")
+
+
+class BasaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({status_string(status)})")
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the in-tree library once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise BasaError(-1, f"{LIB_PATH} is missing; build it with `python -m sparse_attention_dit_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    lib.basa_window_attn_fwd.argtypes = [vp, vp, vp, vp] + [i] * 13 + [vp]
+    lib.basa_window_attn_fwd.restype = i
+    lib.basa_full_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
+    lib.basa_full_attn_fwd.restype = i
+    lib.basa_window_perm.argtypes = [i] * 9 + [vp, vp]
+    lib.basa_window_perm.restype = i
+    lib.basa_status_string.argtypes = [i]
+    lib.basa_status_string.restype = ctypes.c_char_p
+    lib.basa_version.argtypes = []
+    lib.basa_version.restype = i
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    if status == -1:
+        return "library not built"
+    return load().basa_status_string(int(status)).decode()
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise BasaError(3, f"unsupported tensor dtype {t.dtype}")
+
+
+def _check_tensors(q, k, v, out):
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if not t.is_cuda:
+            raise BasaError(1, f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise BasaError(2, f"{name} must be contiguous")
+        if t.dim() != 4:
+            raise BasaError(2, f"{name} must be [B, heads, N, head_dim]")
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise BasaError(2, f"{name} shape/dtype {tuple(t.shape)}/{t.dtype} differs from q")
+
+
+def window_attn_fwd(q, k, v, out, grid, window, shift, stream=None) -> None:
+    """Shifted local-window attention into ``out`` (all [B, heads, T*H*W, head_dim])."""
+    _check_tensors(q, k, v, out)
+    B, H_, N, d = q.shape
+    T, H, W = (int(x) for x in grid)
+    wt, wh, ww = (int(x) for x in window)
+    st, sh, sw = (int(x) for x in shift)
+    if T * H * W != N:
+        raise BasaError(2, f"grid {grid} holds {T * H * W} tokens, tensors hold {N}")
+    rc = load().basa_window_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H_, T, H, W,
+                                     wt, wh, ww, st, sh, sw, d, _dtype_code(q), _stream_handle(stream))
+    if rc != 0:
+        raise BasaError(rc, "basa_window_attn_fwd")
+
+
+def full_attn_fwd(q, k, v, out, stream=None) -> None:
+    """Dense attention baseline (same kernel, window = whole sequence)."""
+    _check_tensors(q, k, v, out)
+    B, H_, N, d = q.shape
+    rc = load().basa_full_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H_, N, d,
+                                   _dtype_code(q), _stream_handle(stream))
+    if rc != 0:
+        raise BasaError(rc, "basa_full_attn_fwd")
+
+
+def window_perm(grid, window, shift, perm, stream=None) -> None:
+    """Write the window membership table (int32 device tensor of T*H*W entries)."""
+    import torch
+    if not perm.is_cuda or perm.dtype != torch.int32 or not perm.is_contiguous():
+        raise BasaError(2, "perm must be a contiguous int32 device tensor")
+    T, H, W = (int(x) for x in grid)
+    if perm.numel() != T * H * W:
+        raise BasaError(2, f"perm holds {perm.numel()} entries, grid has {T * H * W}")
+    wt, wh, ww = (int(x) for x in window)
+    st, sh, sw = (int(x) for x in shift)
+    rc = load().basa_window_perm(T, H, W, wt, wh, ww, st, sh, sw, perm.data_ptr(), _stream_handle(stream))
+    if rc != 0:
+        raise BasaError(rc, "basa_window_perm")
+
+
+def version() -> int:
+    return int(load().basa_version())

@@ -1,0 +1,111 @@
+// C ABI of the shifted local-window attention library: argument validation, shift
+// reduction, kernel selection. Every check runs before the first HIP call, so a bad
+// argument never reaches the device. Declarations and contracts: include/basa.h.
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/basa.h"
+#include "attn_launch.hpp"
+#include "index_map.hpp"
+
+namespace {
+
+constexpr int64_t kInt32Max = 0x7fffffff;
+
+int reduce_mod(int s, int n) {
+  const int r = s % n;  // in (-n, n)
+  return r < 0 ? r + n : r;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlaps(const void* a, const void* b, int64_t bytes) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + uint64_t(bytes) && y < x + uint64_t(bytes);
+}
+
+int check_grid(int T, int H, int W, int wt, int wh, int ww) {
+  if (T <= 0 || H <= 0 || W <= 0 || wt <= 0 || wh <= 0 || ww <= 0) return BASA_ERR_SHAPE;
+  if (T % wt || H % wh || W % ww) return BASA_ERR_SHAPE;
+  if (int64_t(T) * H * W > kInt32Max) return BASA_ERR_OVERFLOW;
+  return BASA_OK;
+}
+
+int run_attention(const void* q, const void* k, const void* v, void* out, int B, int heads, int T, int H, int W,
+                  int wt, int wh, int ww, int st, int sh, int sw, int head_dim, int dtype, hipStream_t stream) {
+  if (!q || !k || !v || !out) return BASA_ERR_NULL;
+  if (dtype != BASA_DTYPE_F32 && dtype != BASA_DTYPE_BF16) return BASA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return BASA_ERR_UNSUPPORTED;
+  if (B <= 0 || heads <= 0) return BASA_ERR_SHAPE;
+  const int g = check_grid(T, H, W, wt, wh, ww);
+  if (g != BASA_OK) return g;
+  const int64_t N = int64_t(T) * H * W;
+  const int64_t bh = int64_t(B) * heads;
+  if (bh > kInt32Max || N * head_dim > kInt32Max) return BASA_ERR_OVERFLOW;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return BASA_ERR_ALIGN;
+  const int64_t elem = dtype == BASA_DTYPE_BF16 ? 2 : 4;
+  const int64_t bytes = bh * N * head_dim * elem;
+  if (overlaps(out, q, bytes) || overlaps(out, k, bytes) || overlaps(out, v, bytes)) return BASA_ERR_ALIAS;
+
+  basa::AttnParams p;
+  p.map = basa::make_winmap(T, H, W, wt, wh, ww, reduce_mod(st, T), reduce_mod(sh, H), reduce_mod(sw, W));
+  p.wtok = wt * wh * ww;
+  p.n_win = int32_t(N / p.wtok);
+  p.q_tiles = 0;
+  p.kv_tiles = 0;
+  p.heads_total = int32_t(bh);
+  p.head_stride = N * head_dim;
+  p.scale_log2 = float(1.4426950408889634 / sqrt(double(head_dim)));
+  const hipError_t e =
+      basa::launch_window_attention(q, k, v, out, p, head_dim, dtype == BASA_DTYPE_BF16, stream);
+  if (e == hipErrorInvalidConfiguration) return BASA_ERR_OVERFLOW;
+  return e == hipSuccess ? BASA_OK : BASA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int basa_window_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int heads, int T, int H,
+                         int W, int wt, int wh, int ww, int st, int sh, int sw, int head_dim, int dtype,
+                         hipStream_t stream) {
+  return run_attention(q, k, v, out, B, heads, T, H, W, wt, wh, ww, st, sh, sw, head_dim, dtype, stream);
+}
+
+int basa_full_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int heads, int N,
+                       int head_dim, int dtype, hipStream_t stream) {
+  return run_attention(q, k, v, out, B, heads, 1, 1, N, 1, 1, N, 0, 0, 0, head_dim, dtype, stream);
+}
+
+int basa_window_perm(int T, int H, int W, int wt, int wh, int ww, int st, int sh, int sw, int32_t* perm,
+                     hipStream_t stream) {
+  if (!perm) return BASA_ERR_NULL;
+  const int g = check_grid(T, H, W, wt, wh, ww);
+  if (g != BASA_OK) return g;
+  if (!aligned(perm, 4)) return BASA_ERR_ALIGN;
+  const basa::WinMap map =
+      basa::make_winmap(T, H, W, wt, wh, ww, reduce_mod(st, T), reduce_mod(sh, H), reduce_mod(sw, W));
+  const int32_t total = T * H * W;
+  const hipError_t e = basa::launch_window_perm(map, wt * wh * ww, total, perm, stream);
+  return e == hipSuccess ? BASA_OK : BASA_ERR_HIP;
+}
+
+const char* basa_status_string(int status) {
+  switch (status) {
+    case BASA_OK: return "ok";
+    case BASA_ERR_NULL: return "a required pointer is NULL";
+    case BASA_ERR_SHAPE: return "non-positive size, or the window does not divide the grid";
+    case BASA_ERR_UNSUPPORTED: return "unsupported dtype or head_dim (supported: f32/bf16 x 64/128)";
+    case BASA_ERR_ALIAS: return "out overlaps q, k or v";
+    case BASA_ERR_OVERFLOW: return "size exceeds the 32-bit per-head indexing";
+    case BASA_ERR_HIP: return "HIP launch error";
+    case BASA_ERR_ALIGN: return "tensor pointer is not 16-byte aligned (perm: 4-byte)";
+    default: return "unknown status";
+  }
+}
+
+int basa_version(void) { return (1 << 16) | 0; }
+
+}  // extern "C"

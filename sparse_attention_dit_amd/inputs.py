@@ -34,12 +34,16 @@ def bf16_bits_to_float32(bits: np.ndarray) -> np.ndarray:
 
 class Tensors:
     """One drawn tensor set: ``dev`` holds what goes to the device (float32 array, or
-    uint16 bf16 bits), ``f64`` holds the identical values as float64 for the oracle."""
+    uint16 bf16 bits); ``exact`` holds the identical values as float32 arrays (bf16
+    values are exactly representable); ``f64(name)`` upcasts one of them to float64."""
 
-    def __init__(self, dtype: str, dev: dict, f64: dict):
+    def __init__(self, dtype: str, dev: dict, exact: dict):
         self.dtype = dtype
         self.dev = dev
-        self.f64 = f64
+        self.exact = exact
+
+    def f64(self, name: str) -> np.ndarray:
+        return self.exact[name].astype(np.float64)
 
 
 def draw_qkv(shape, dtype: str, seed: int, q_scale: float = 1.0) -> Tensors:
@@ -56,29 +60,43 @@ def draw_qkv(shape, dtype: str, seed: int, q_scale: float = 1.0) -> Tensors:
         raw[name] = rng.standard_normal(tuple(shape), dtype=np.float32)
     if q_scale != 1.0:
         raw["q"] = (raw["q"] * np.float32(q_scale)).astype(np.float32)
-    dev, f64 = {}, {}
+    dev, exact = {}, {}
     for name, a in raw.items():
         if dtype == "bf16":
             bits = round_to_bf16_bits(a)
             dev[name] = bits
-            f64[name] = bf16_bits_to_float32(bits).astype(np.float64)
+            exact[name] = bf16_bits_to_float32(bits)
         else:
             dev[name] = a
-            f64[name] = a.astype(np.float64)
-    return Tensors(dtype, dev, f64)
+            exact[name] = a
+    return Tensors(dtype, dev, exact)
 
 
 def from_float_arrays(arrays: dict, dtype: str) -> Tensors:
     """Wrap caller-built float arrays (structured probes: one-hot V, zero Q, ...) so that
     both sides again see identical values. Values are rounded to bf16 when dtype is bf16."""
-    dev, f64 = {}, {}
+    dev, exact = {}, {}
     for name, a in arrays.items():
         a32 = np.ascontiguousarray(a, dtype=np.float32)
         if dtype == "bf16":
             bits = round_to_bf16_bits(a32)
             dev[name] = bits
-            f64[name] = bf16_bits_to_float32(bits).astype(np.float64)
+            exact[name] = bf16_bits_to_float32(bits)
         else:
             dev[name] = a32
-            f64[name] = a32.astype(np.float64)
-    return Tensors(dtype, dev, f64)
+            exact[name] = a32
+    return Tensors(dtype, dev, exact)
+
+
+def draw_qkv_device(shape, dtype: str, seed: int, device="cuda"):
+    """Seeded q, k, v drawn directly in device memory (torch's generator, N(0,1)),
+    for sizes whose host copies would not fit; callers copy back only the rows the
+    oracle needs. Returns a dict of device tensors of ``dtype`` ("bf16" or "f32")."""
+    import torch
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    out = {}
+    for name in ("q", "k", "v"):
+        out[name] = torch.randn(tuple(shape), generator=gen, device=device, dtype=torch.float32).to(tdt)
+    return out

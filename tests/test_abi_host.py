@@ -1,0 +1,117 @@
+"""Host-side checks of the C ABI and of the library's index map (no GPU needed).
+
+* the built library loads and exports every function include/basa.h declares;
+* every argument error returns its status code before any HIP call is made;
+* the index map header, compiled for the host, reproduces the oracle's membership table
+  bit for bit, and its division by invariant integers matches '/'.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle import basa_oracle as O
+from sparse_attention_dit_amd import _lib
+from sparse_attention_dit_amd.configs import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "basa.h")
+CSRC = os.path.join(ROOT, "sparse_attention_dit_amd", "csrc")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(basa_\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_and_binding_agree():
+    declared = _declared_functions()
+    assert set(declared) == set(_lib.SYMBOLS), declared
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = set(re.findall(r"\sT\s(\w+)", nm.stdout))
+    for name in _declared_functions():
+        assert name in exported, name
+
+
+def test_status_strings():
+    for code in range(8):
+        s = _lib.status_string(code)
+        assert s and s != "unknown status"
+    assert _lib.status_string(99) == "unknown status"
+    assert _lib.version() >> 16 == 1
+
+
+# fake, aligned, distinct device addresses: every call below must fail validation before
+# the library touches HIP, so they are never dereferenced
+A, Bp, Cp, D = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+def _win(q=A, k=Bp, v=Cp, out=D, B=1, heads=2, grid=(1, 16, 16), window=(1, 8, 8), shift=(0, 4, 4),
+         head_dim=64, dtype=0):
+    return _lib.load().basa_window_attn_fwd(q, k, v, out, B, heads, *grid, *window, *shift, head_dim, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(out=None), 1),
+    (dict(B=0), 2), (dict(heads=-1), 2), (dict(grid=(1, 0, 16)), 2), (dict(window=(1, 8, 0)), 2),
+    (dict(window=(1, 6, 8)), 2), (dict(grid=(3, 16, 16), window=(2, 8, 8)), 2),
+    (dict(head_dim=96), 3), (dict(head_dim=256), 3), (dict(dtype=2), 3), (dict(dtype=-1), 3),
+    (dict(out=A), 4), (dict(out=Bp + 64), 4), (dict(q=D + 128 * 64 * 4 - 16), 4),
+    (dict(grid=(1, 65536, 65536), window=(1, 1, 1)), 5),
+    (dict(grid=(1, 4096, 8192), window=(1, 1, 1), head_dim=128), 5),
+    (dict(B=65536, heads=65536), 5),
+    (dict(q=A + 8), 7), (dict(out=D + 4), 7),
+])
+def test_argument_errors_return_codes(kw, code):
+    assert _win(**kw) == code
+
+
+def test_full_and_perm_argument_errors():
+    lib = _lib.load()
+    assert lib.basa_full_attn_fwd(None, Bp, Cp, D, 1, 1, 64, 64, 1, None) == 1
+    assert lib.basa_full_attn_fwd(A, Bp, Cp, D, 1, 1, 0, 64, 1, None) == 2
+    assert lib.basa_full_attn_fwd(A, Bp, Cp, D, 1, 1, 64, 80, 1, None) == 3
+    assert lib.basa_full_attn_fwd(A, Bp, Cp, A, 1, 1, 64, 64, 1, None) == 4
+    assert lib.basa_window_perm(1, 16, 16, 1, 8, 8, 0, 0, 0, None, None) == 1
+    assert lib.basa_window_perm(1, 16, 16, 1, 5, 8, 0, 0, 0, A, None) == 2
+    assert lib.basa_window_perm(1, 16, 16, 1, 8, 8, 0, 0, 0, A + 2, None) == 7
+
+
+@pytest.fixture(scope="module")
+def index_tool(tmp_path_factory):
+    exe = str(tmp_path_factory.mktemp("idx") / "index_map_check")
+    subprocess.run(["g++", "-O2", "-std=c++17", "-Wall", "-I", CSRC,
+                    os.path.join(ROOT, "tests", "host", "index_map_check.cpp"), "-o", exe], check=True)
+    return exe
+
+
+def test_fastdiv_matches_division(index_tool):
+    res = subprocess.run([index_tool, "fastdiv"], capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, res.stdout + res.stderr
+
+
+CASES = [(w.grid, w.window, s) for w in WORKLOADS for s in w.shifts] + [
+    ((21, 30, 52), (21, 15, 26), (5, -7, 40)),
+    ((6, 6, 6), (3, 2, 3), (-1, -5, 8)),
+    ((1, 1, 4096), (1, 1, 4096), (0, 0, 0)),       # the dense baseline's degenerate map
+    ((2, 3, 5), (1, 1, 1), (1, 1, 1)),
+]
+
+
+@pytest.mark.parametrize("grid,window,shift", CASES)
+def test_index_map_header_matches_oracle_table(index_tool, tmp_path, grid, window, shift):
+    out = str(tmp_path / "t.bin")
+    subprocess.run([index_tool, "table", *map(str, grid), *map(str, window), *map(str, shift), out], check=True)
+    got = np.fromfile(out, dtype=np.int32)
+    ref = O.window_members(grid, window, shift).ravel()
+    assert np.array_equal(got, ref)

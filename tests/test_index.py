@@ -119,3 +119,12 @@ def test_table3_density_golden():
         sparsity = 1.0 - (2 * M + G) / N
         assert round(100 * sparsity, 2) == row["sparsity_percent"], row
         assert n_win == 16
+
+
+def test_members_of_agrees_with_table():
+    for grid, window, s in [((21, 30, 52), (7, 15, 26), (3, 7, 13)), ((1, 64, 64), (1, 16, 16), (0, 8, 8)),
+                            ((6, 6, 6), (3, 2, 3), (-1, -5, 8))]:
+        table = O.window_members(grid, window, s)
+        win, _ = forward_map(grid, window, O.reduce_shift(grid, s))
+        for p in np.random.default_rng(0).choice(int(np.prod(grid)), 50, replace=False):
+            assert np.array_equal(O.members_of(grid, window, s, p), table[win[p]])

@@ -1,0 +1,205 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the same
+seeded inputs.
+
+Bars: bf16 rel-L2 <= 5e-3 and max-abs <= 2e-2; fp32 <= 1e-5 (both); window membership
+and indexing bit-exact. Small cases compare every output element; the five full-size
+workloads compare sampled rows (each computed on its own by the oracle) in exactly the
+launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import assert_parity, log_case, to_device, to_host
+from oracle import basa_oracle as O
+from sparse_attention_dit_amd import _lib, inputs
+from sparse_attention_dit_amd.configs import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+
+def run_window(dev, grid, window, shift):
+    out = torch.empty_like(dev["q"])
+    _lib.window_attn_fwd(dev["q"], dev["k"], dev["v"], out, grid, window, shift)
+    torch.cuda.synchronize()
+    return out
+
+
+def run_full(dev):
+    out = torch.empty_like(dev["q"])
+    _lib.full_attn_fwd(dev["q"], dev["k"], dev["v"], out)
+    torch.cuda.synchronize()
+    return out
+
+
+# name, dtype, B, heads, head_dim, grid, window, shifts, seed
+SMALL = [
+    ("tiny-2d-f32", "f32", 1, 2, 64, (1, 16, 16), (1, 8, 8), [(0, 0, 0), (0, 4, 4)], 1),
+    ("2d-ragged-w240", "bf16", 1, 3, 128, (1, 24, 40), (1, 12, 20), [(0, 0, 0), (0, 5, -7)], 101),
+    ("3d-w2730-ragged", "bf16", 1, 2, 128, (7, 30, 26), (7, 15, 26), [(0, 0, 0), (3, 7, 13)], 102),
+    ("3d-w60-b2", "bf16", 2, 2, 128, (4, 10, 12), (2, 5, 6), [(1, 2, 3), (-1, -2, -3)], 103),
+    ("2d-d64", "bf16", 1, 2, 64, (1, 32, 32), (1, 16, 16), [(0, 0, 0), (0, 8, 8)], 104),
+    ("3d-d64-ragged", "bf16", 1, 2, 64, (3, 10, 14), (3, 5, 7), [(2, 4, 6)], 110),
+    ("video-full-T", "bf16", 1, 2, 128, (5, 12, 16), (5, 6, 8), [(0, 3, 4), (2, 1, 7)], 105),
+    ("f32-d128", "f32", 1, 2, 128, (2, 8, 12), (2, 4, 6), [(1, 1, 1)], 106),
+    ("f32-ragged-w45", "f32", 1, 2, 64, (3, 6, 10), (3, 3, 5), [(1, 2, 3)], 109),
+    ("window-1x1x1", "bf16", 1, 2, 128, (1, 8, 8), (1, 1, 1), [(0, 3, 5)], 107),
+    ("window-is-grid", "bf16", 1, 2, 128, (2, 6, 10), (2, 6, 10), [(1, 3, 5)], 108),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_cases_every_element(case):
+    name, dtype, B, heads, d, grid, window, shifts, seed = case
+    N = int(np.prod(grid))
+    t = inputs.draw_qkv((B, heads, N, d), dtype, seed)
+    dev = to_device(t)
+    q, k, v = t.f64("q"), t.f64("k"), t.f64("v")
+    for s in shifts:
+        log_case(name, "seed", seed, "shape", (B, heads, N, d), "shift", s, "basa_window_attn_fwd")
+        got = to_host(run_window(dev, grid, window, s))
+        ref = O.window_attention(q, k, v, grid, window, s)
+        assert_parity(got, ref, dtype, f"{name} shift {s}")
+
+
+def test_peaky_logits():
+    grid, window, s = (1, 24, 40), (1, 12, 20), (0, 5, -7)
+    t = inputs.draw_qkv((1, 2, 960, 128), "bf16", seed=120, q_scale=8.0)
+    dev = to_device(t)
+    log_case("peaky q*8", "seed 120", "shift", s)
+    got = to_host(run_window(dev, grid, window, s))
+    ref = O.window_attention(t.f64("q"), t.f64("k"), t.f64("v"), grid, window, s)
+    assert_parity(got, ref, "bf16", "peaky logits")
+
+
+def _sample_rows(N, seed, grid, window, shift, count=96):
+    rng = np.random.default_rng(1000 + seed)
+    rows = set(rng.choice(N, size=count, replace=False).tolist())
+    rows |= {0, N - 1}
+    table = O.window_members(grid, window, shift)
+    rows |= {int(table[0, 0]), int(table[0, -1]), int(table[-1, 0]), int(table[-1, -1])}
+    return np.array(sorted(rows))
+
+
+@pytest.fixture(scope="module")
+def workload_inputs():
+    cache = {}
+
+    def get(w):
+        if w.name not in cache:
+            cache.clear()
+            t = inputs.draw_qkv(w.shape, w.dtype, w.seed)
+            cache[w.name] = (t, to_device(t))
+        return cache[w.name]
+    yield get
+    cache.clear()
+
+
+@pytest.mark.parametrize("w", WORKLOADS, ids=lambda w: w.name)
+def test_workload_window_parity(w, workload_inputs):
+    t, dev = workload_inputs(w)
+    for s in w.shifts:
+        log_case(w.name, "seed", w.seed, "shape", w.shape, "shift", s, "basa_window_attn_fwd")
+        out = run_window(dev, w.grid, w.window, s)
+        if w.tokens <= 4096 and w.heads * w.tokens * w.window_tokens <= 2 ** 26:
+            ref = O.window_attention(t.f64("q"), t.f64("k"), t.f64("v"), w.grid, w.window, s)
+            got = to_host(out)
+        else:
+            rows = _sample_rows(w.tokens, w.seed, w.grid, w.window, s)
+            ref = O.window_attention_rows(t.exact["q"], t.exact["k"], t.exact["v"], w.grid, w.window, s, rows)
+            got = to_host(out[:, :, torch.from_numpy(rows).cuda()])
+        assert_parity(got, ref, w.dtype, f"{w.name} shift {s}")
+
+
+@pytest.mark.parametrize("w", WORKLOADS, ids=lambda w: w.name)
+def test_workload_membership_bit_exact(w):
+    for s in w.shifts:
+        log_case(w.name, "shift", s, "basa_window_perm")
+        perm = torch.empty(w.tokens, dtype=torch.int32, device="cuda")
+        _lib.window_perm(w.grid, w.window, s, perm)
+        torch.cuda.synchronize()
+        assert np.array_equal(perm.cpu().numpy(), O.window_members(w.grid, w.window, s).ravel())
+
+
+def test_membership_extra_shapes():
+    for grid, window, s in [((6, 6, 6), (3, 2, 3), (-1, -5, 8)), ((1, 1, 4096), (1, 1, 4096), (0, 0, 0)),
+                            ((21, 30, 52), (21, 15, 26), (5, -7, 40)), ((2, 3, 5), (1, 1, 1), (7, 7, 7))]:
+        log_case("perm", grid, window, s)
+        perm = torch.empty(int(np.prod(grid)), dtype=torch.int32, device="cuda")
+        _lib.window_perm(grid, window, s, perm)
+        torch.cuda.synchronize()
+        assert np.array_equal(perm.cpu().numpy(), O.window_members(grid, window, s).ravel())
+
+
+@pytest.mark.parametrize("w", [WORKLOADS[2], WORKLOADS[3]], ids=lambda w: w.name)
+def test_one_hot_probe_reads_membership_exactly(w):
+    """q = k = 0 gives uniform weights 1/W inside each window; with v[:, c] one-hot at
+    token t_c the output is [win(i) == win(t_c)] / W, exact in bf16 for W = 1024."""
+    rng = np.random.default_rng(77)
+    B, H, N, d = w.shape
+    heads = 2
+    probe = rng.choice(N, size=d, replace=False)
+    vv = np.zeros((B, heads, N, d), dtype=np.float32)
+    vv[:, :, probe, np.arange(d)] = 1.0
+    zeros = np.zeros_like(vv)
+    t = inputs.from_float_arrays({"q": zeros, "k": zeros, "v": vv}, "bf16")
+    dev = to_device(t)
+    for s in w.shifts:
+        log_case(w.name, "one-hot probe", "shift", s)
+        got = run_window(dev, w.grid, w.window, s).float().cpu().numpy()
+        table = O.window_members(w.grid, w.window, s)
+        owner = np.empty(N, dtype=np.int64)
+        for m, members in enumerate(table):
+            owner[members] = m
+        expect = (owner[:, None] == owner[probe][None, :]).astype(np.float32) / w.window_tokens
+        for b in range(B):
+            for h in range(heads):
+                assert np.array_equal(got[b, h], expect)
+
+
+def test_shift_equivalences_are_bitwise():
+    grid, window = (7, 30, 26), (7, 15, 26)
+    t = inputs.draw_qkv((1, 2, 5460, 128), "bf16", seed=130)
+    dev = to_device(t)
+    base = run_window(dev, grid, window, (3, 7, 13))
+    for s in [(3 + 7, 7 - 15, 13 + 26), (3 - 7, 7 + 30, 13 - 52), (-4, -23, -39)]:
+        log_case("shift equivalence", s)
+        assert torch.equal(run_window(dev, grid, window, s), base), s
+    other = run_window(dev, grid, window, (3, 8, 13))
+    assert not torch.equal(other, base)
+
+
+def test_full_attention_small_every_element():
+    for dtype, seed, shape in [("f32", 140, (1, 2, 256, 64)), ("bf16", 141, (1, 2, 1000, 128)),
+                               ("bf16", 142, (2, 1, 300, 64))]:
+        t = inputs.draw_qkv(shape, dtype, seed)
+        dev = to_device(t)
+        log_case("full attention", dtype, shape)
+        got = to_host(run_full(dev))
+        ref = O.full_attention(t.f64("q"), t.f64("k"), t.f64("v"))
+        assert_parity(got, ref, dtype, f"full {dtype} {shape}")
+
+
+@pytest.mark.parametrize("w", [WORKLOADS[1], WORKLOADS[2], WORKLOADS[4]], ids=lambda w: w.name)
+def test_full_attention_workload_sampled(w, workload_inputs):
+    t, dev = workload_inputs(w)
+    log_case(w.name, "basa_full_attn_fwd", w.shape)
+    out = run_full(dev)
+    rows = np.array(sorted(set(np.random.default_rng(2000 + w.seed).choice(w.tokens, 48, replace=False).tolist())
+                           | {0, w.tokens - 1}))
+    ref = O.full_attention_rows(t.exact["q"], t.exact["k"], t.exact["v"], rows)
+    got = to_host(out[:, :, torch.from_numpy(rows).cuda()])
+    assert_parity(got, ref, w.dtype, f"full {w.name}")
+
+
+def test_window_equal_grid_matches_full_attention_path():
+    """window == grid under any shift is dense attention: the windowed entry point and
+    the dense baseline must agree (same kernel, the shift only permutes the keys)."""
+    grid = (3, 8, 10)
+    t = inputs.draw_qkv((1, 2, 240, 128), "bf16", seed=150)
+    dev = to_device(t)
+    full = to_host(run_full(dev))
+    for s in [(0, 0, 0), (1, 3, 7)]:
+        log_case("window=grid", s)
+        got = to_host(run_window(dev, grid, grid, s))
+        assert_parity(got, full, "bf16", f"window=grid shift {s} vs full")
