@@ -84,41 +84,67 @@ __device__ __forceinline__ int key_perm(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
-template <int D, int NW, int QB>
-struct Bf16Cfg {
-  static constexpr int BN = 64;                 // keys per K/V tile
-  static constexpr int BM = NW * 32 * QB;       // query rows per workgroup
-  static constexpr int NT = NW * 64;            // threads
-  static constexpr int KS = D + 8;              // K row stride in LDS (elements)
-  static constexpr int VS = BN + 8;             // Vt row stride in LDS (elements)
-  static constexpr int VSKEW = 64;              // extra offset of Vt rows d >= D/2
-  static constexpr int DK = D / 16;             // k-steps of S^T per key block
-  static constexpr int DB = D / 32;             // 32-row d blocks of O^T
-  static constexpr int KCH = D / 8;             // 16-byte chunks per row
-  static constexpr int RK = BN * KCH / NT;      // K chunks per thread
-  static constexpr int RV = BN * KCH / NT;      // V rows per thread (one 8-wide d chunk each)
-  static constexpr int VKG = BN / RV;           // key groups of the V transpose
-  static_assert(RK >= 1 && RV >= 1 && (RV & (RV - 1)) == 0 && RV <= 8, "tile/thread mismatch");
-  static constexpr int KS_BYTES = BN * KS * 2;
-  static constexpr int VT_BYTES = (D * VS + VSKEW) * 2;
+// LDS tile layout (one K tile or one V tile of BN rows x D bf16).
+// Rows are grouped RPG at a time (RPG * D * 2 = 1 KB, the bytes one wave-wide 16-byte
+// load moves). Inside a group the 16-byte chunks are interleaved by row:
+//   byte(row, chunk) = (row / RPG) * RG + slot(chunk) * RPG * 16 + (row % RPG) * 16
+// with groups RG = 1 KB + RPG * 16 apart. One wave-wide direct global->LDS load fills one
+// group (lane j -> slot j / RPG, row j % RPG: 16-byte pieces of RPG whole rows, so the
+// global reads stay row-contiguous). The skew between groups makes the 16 rows that an
+// MFMA operand read touches land in 16 distinct bank groups; slot() swaps neighbouring
+// chunks in the upper half of V so the two halves read by one transpose group differ too.
+template <int D>
+struct TileLayout {
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  static constexpr int RPG = 1024 / ROW_BYTES;       // rows per group (4 for D=128, 8 for D=64)
+  static constexpr int CS = RPG * 16;                // chunk-slot stride inside a group
+  static constexpr int RG = 1024 + CS;               // group stride
+  __host__ __device__ static constexpr int v_slot(int c) { return c >= CPR / 2 ? (c ^ 1) : c; }
 };
 
-__device__ __forceinline__ int vt_row_offset(int d, int D, int VS, int VSKEW) {
-  return d * VS + (d >= D / 2 ? VSKEW : 0);
+template <int D, int NW>
+struct Bf16Cfg {
+  using L = TileLayout<D>;
+  static constexpr int BN = 64;                       // keys per K/V tile
+  static constexpr int BM = NW * 32;                  // query rows per workgroup (32 per wave)
+  static constexpr int NT = NW * 64;
+  static constexpr int GROUPS = BN / L::RPG;          // row groups per tile
+  static constexpr int TILE_BYTES = GROUPS * L::RG;   // one K or V tile in LDS
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K tile then V tile
+  static constexpr int STAGES = 2;
+  static constexpr int LOADS = GROUPS / NW;           // wave-wide loads per tensor per wave
+  static constexpr int DK = D / 16;                   // MFMA k-steps of S^T per key block
+  static constexpr int DB = D / 32;                   // 32-row d blocks of O^T
+  static_assert(LOADS >= 1 && LOADS * NW == GROUPS, "tile/wave mismatch");
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+};
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // raw buffer, 32-bit data format (gfx9 descriptor word 3); reads past `bytes` return 0
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-template <int D, int NW, int QB>
-__global__ __launch_bounds__(NW * 64) void win_attn_bf16_kernel(const uint16_t* __restrict__ q,
-                                                                 const uint16_t* __restrict__ k,
-                                                                 const uint16_t* __restrict__ v,
-                                                                 uint16_t* __restrict__ out,
-                                                                 AttnParams p) {
-  using C = Bf16Cfg<D, NW, QB>;
-  constexpr int BN = C::BN, BM = C::BM, NT = C::NT, KS = C::KS, VS = C::VS, VSKEW = C::VSKEW;
-  constexpr int DK = C::DK, DB = C::DB, KCH = C::KCH, RK = C::RK, RV = C::RV, VKG = C::VKG;
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void win_attn_bf16_kernel(const uint16_t* __restrict__ q,
+                                                                    const uint16_t* __restrict__ k,
+                                                                    const uint16_t* __restrict__ v,
+                                                                    uint16_t* __restrict__ out,
+                                                                    AttnParams p) {
+  using C = Bf16Cfg<D, NW>;
+  using L = TileLayout<D>;
+  constexpr int BN = C::BN, BM = C::BM, DK = C::DK, DB = C::DB;
+  constexpr int RPG = L::RPG, CS = L::CS, RG = L::RG, CPR = L::CPR;
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VS + VSKEW];
+  // Two stages as separate objects: with the stage fixed at compile time in each half of
+  // the unrolled tile loop, the compiler can tell that the transpose reads of one stage do
+  // not alias the DMA into the other and does not make them wait for it.
+  __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char stage1[C::STAGE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -129,138 +155,89 @@ __global__ __launch_bounds__(NW * 64) void win_attn_bf16_kernel(const uint16_t* 
   const TileId tile = decode_tile(p);
   const int64_t base = int64_t(tile.bh) * p.head_stride;
   const WinOrigin org = window_origin(p.map, uint32_t(tile.win));
-  const uint16_t* qh = q + base;
-  const uint16_t* kh = k + base;
-  const uint16_t* vh = v + base;
+  const uint32_t head_bytes = uint32_t(p.head_stride) * 2u;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + base, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + base, head_bytes);
+
+  // ---- K/V tile loads: wave `wave` fills row groups wave*LOADS .. +LOADS-1 of both tiles.
+  // Lane j moves 16 bytes: chunk slot j / RPG of row (group*RPG + j % RPG).
+  const int ld_slot = lane / RPG;
+  const int ld_row = lane % RPG;
+  const uint32_t k_chunk_off = uint32_t(ld_slot) * 16u;
+  const uint32_t v_chunk_off = uint32_t(L::v_slot(ld_slot)) * 16u;
+  auto issue_tile = [&](int t, char* st) {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int g = wave * C::LOADS + i;
+      const int local = t * BN + g * RPG + ld_row;
+      uint32_t row_off = 0xffffff00u;  // rows past the window read as zeros
+      if (local < p.wtok) row_off = uint32_t(token_of(p.map, org, uint32_t(local))) * uint32_t(L::ROW_BYTES);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void_t*)(st + g * RG), 16, row_off + k_chunk_off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_t*)(st + C::TILE_BYTES + g * RG), 16,
+                                               row_off + v_chunk_off, 0, 0, 0);
+    }
+  };
+
+  issue_tile(0, stage0);
 
   // ---- Q fragments (B operand of S^T): lane holds d = hh*D/2 + 8*kk .. +7 of its row.
-  bf16x8_t qf[QB][DK];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = tile.qtile * BM + (wave * QB + qb) * 32 + l32;
+  bf16x8_t qf[DK];
+  {
+    const int row = tile.qtile * BM + wave * 32 + l32;
     if (row < p.wtok) {
       const int tok = token_of(p.map, org, uint32_t(row));
-      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(qh + int64_t(tok) * D + hh * (D / 2));
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(q + base + int64_t(tok) * D + hh * (D / 2));
 #pragma unroll
-      for (int kk = 0; kk < DK; ++kk) qf[qb][kk] = __builtin_bit_cast(bf16x8_t, src[kk]);
+      for (int kk = 0; kk < DK; ++kk) qf[kk] = __builtin_bit_cast(bf16x8_t, src[kk]);
     } else {
 #pragma unroll
-      for (int kk = 0; kk < DK; ++kk) qf[qb][kk] = __builtin_bit_cast(bf16x8_t, u32x4_t{0, 0, 0, 0});
+      for (int kk = 0; kk < DK; ++kk) qf[kk] = __builtin_bit_cast(bf16x8_t, u32x4_t{0, 0, 0, 0});
     }
   }
 
-  // ---- K/V tile staging: global -> registers (prefetch) -> LDS.
-  const int k_col = tid % KCH;           // K: row-major chunks, 16 lanes per 256-byte row
-  const int k_row0 = tid / KCH;
-  constexpr int K_ROW_STEP = NT / KCH;
-  const int v_kg = tid % VKG;            // V: RV consecutive keys x 8 d per thread
-  const int v_dg = tid / VKG;
-  u32x4_t kreg[RK];
-  u32x4_t vreg[RV];
+  // ---- per-lane LDS read bases (all per-step offsets below are compile-time constants)
+  // K (A operand of S^T): row 32*kb + key_perm(l32), chunk hh*CPR/2 + kk.
+  const int krow = key_perm(l32);
+  const int k_rd = (krow / RPG) * RG + (krow % RPG) * 16 + hh * (CPR / 2) * CS;
+  // V^T (A operand of O^T) by transpose reads: in each 16-lane group lane i supplies the
+  // address of 4 consecutive d of key row (i / 4) and receives one d of 4 keys. Lane
+  // (g, i, hh) of block db reads d-chunk 2*db + g (lower half of d) for i%4 in {0, 2} and
+  // CPR/2 + 2*db + g (upper half) for i%4 in {1, 3}; i%4 in {2, 3} take the chunk's upper 8 bytes.
+  const int vg = l32 >> 4;
+  const int vi = lane & 15;
+  const int v_chunk = ((vi & 1) ? CPR / 2 : 0) + vg;           // + 2*db per block
+  const int v_rd = ((8 * hh) / RPG) * RG + ((8 * hh) % RPG + (vi >> 2)) * 16 + L::v_slot(v_chunk) * CS +
+                   ((vi >> 1) & 1) * 8;
 
-  auto load_tile = [&](int t) {
-    const int local = t * BN + lane;  // lane j computes the token of tile row j
-    const int my_tok = local < p.wtok ? token_of(p.map, org, uint32_t(local)) : -1;
-#pragma unroll
-    for (int i = 0; i < RK; ++i) {
-      const int r = k_row0 + i * K_ROW_STEP;
-      const int tok = __shfl(my_tok, r);
-      kreg[i] = tok >= 0 ? *reinterpret_cast<const u32x4_t*>(kh + int64_t(tok) * D + k_col * 8)
-                         : u32x4_t{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < RV; ++i) {
-      const int r = v_kg * RV + i;
-      const int tok = __shfl(my_tok, r);
-      vreg[i] = tok >= 0 ? *reinterpret_cast<const u32x4_t*>(vh + int64_t(tok) * D + v_dg * 8)
-                         : u32x4_t{0, 0, 0, 0};
-    }
-  };
-
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < RK; ++i) {
-      const int r = k_row0 + i * K_ROW_STEP;
-      *reinterpret_cast<u32x4_t*>(&Ks[r * KS + k_col * 8]) = kreg[i];
-    }
-    // transpose RV rows x 8 d into 8 d-rows x RV keys
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = v_dg * 8 + e;
-      uint16_t* dst = &Vt[vt_row_offset(d, D, VS, VSKEW) + v_kg * RV];
-      const int w = e >> 1;
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      if constexpr (RV == 1) {
-        dst[0] = uint16_t((e & 1) ? (vreg[0][w] >> 16) : (vreg[0][w] & 0xffffu));
-      } else if constexpr (RV == 2) {
-        *reinterpret_cast<uint32_t*>(dst) = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel);
-      } else if constexpr (RV == 4) {
-        u32x2_t x;
-        x[0] = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel);
-        x[1] = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], sel);
-        *reinterpret_cast<u32x2_t*>(dst) = x;
-      } else {
-        u32x4_t x;
-        x[0] = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel);
-        x[1] = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], sel);
-        x[2] = __builtin_amdgcn_perm(vreg[5][w], vreg[4][w], sel);
-        x[3] = __builtin_amdgcn_perm(vreg[7][w], vreg[6][w], sel);
-        *reinterpret_cast<u32x4_t*>(dst) = x;
-      }
-    }
-  };
-
-  // ---- per-lane constant LDS offsets
-  const int k_frag_row = key_perm(l32);  // + 32*kb
-  int v_frag_off[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    const int m = l32;
-    const int dphys = ((m >> 2) & 1) * (D / 2) + 16 * db + 4 * (m >> 3) + (m & 3);
-    v_frag_off[db] = vt_row_offset(dphys, D, VS, VSKEW) + 8 * hh;
-  }
-  // key index (within a 64-key tile) of accumulator register r of key block kb
   auto acc_key = [&](int kb, int r) { return 32 * kb + key_perm(8 * (r >> 2) + 4 * hh + (r & 3)); };
 
-  f32x16_t oacc[QB][DB];
+  f32x16_t oacc[DB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.0f;
-  float m_run[QB], l_run[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -__builtin_inff();
-    l_run[qb] = 0.0f;
-  }
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+  float m_run = -__builtin_inff(), l_run = 0.0f;
   const float c = p.scale_log2;
 
-  load_tile(0);
-  for (int t = 0; t < p.kv_tiles; ++t) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < p.kv_tiles) load_tile(t + 1);
+  // One K/V tile: prefetch tile t+1 into `nxt`, compute tile t from `cur`.
+  auto tile_step = [&](int t, const char* cur, char* nxt) {
+    if (t + 1 < p.kv_tiles) issue_tile(t + 1, nxt);
+    const char* ks = cur;
+    const char* vs = cur + C::TILE_BYTES;
 
     // S^T = K Q^T for 64 keys (two 32-key blocks)
-    f32x16_t sacc[QB][2];
+    f32x16_t sacc[2];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[qb][kb][r] = 0.0f;
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < DK; ++kk) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16x8_t kf =
-            *reinterpret_cast<const bf16x8_t*>(&Ks[(32 * kb + k_frag_row) * KS + hh * (D / 2) + kk * 8]);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          sacc[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][kk], sacc[qb][kb], 0, 0, 0);
+            *reinterpret_cast<const bf16x8_t*>(ks + k_rd + kb * (32 / RPG) * RG + kk * CS);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[kb], 0, 0, 0);
       }
     }
 
@@ -271,33 +248,30 @@ __global__ __launch_bounds__(NW * 64) void win_attn_bf16_kernel(const uint16_t* 
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (acc_key(kb, r) >= lim)
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) sacc[qb][kb][r] = -__builtin_inff();
+          if (acc_key(kb, r) >= lim) sacc[kb][r] = -__builtin_inff();
     }
 
     // online softmax (fp32), P^T packed to bf16 as the B operand of O^T += V^T P^T
-    bf16x8_t pf[QB][4];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = sacc[qb][0][0];
+    bf16x8_t pf[4];
+    {
+      float mx = sacc[0][0];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qb][kb][r]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
       mx = wave_half_max(mx) * c;
-      const bool need = mx > m_run[qb] + 8.0f;
+      const bool need = mx > m_run + 8.0f;
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
-        const float m_new = need ? mx : m_run[qb];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-        m_run[qb] = m_new;
-        l_run[qb] *= alpha;
+        const float m_new = need ? mx : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
       }
-      const float neg_m = -m_run[qb];
+      const float neg_m = -m_run;
       float lsum = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -306,8 +280,8 @@ __global__ __launch_bounds__(NW * 64) void win_attn_bf16_kernel(const uint16_t* 
           u32x4_t packed;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][kb][8 * ch + 2 * e], c, neg_m));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][kb][8 * ch + 2 * e + 1], c, neg_m));
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * ch + 2 * e], c, neg_m));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * ch + 2 * e + 1], c, neg_m));
             // The row sum adds the bf16-rounded p that the PV product uses. The packed word
             // goes through a scalar temporary: bit-casting the vector element directly
             // (packed[e]) makes hipcc 7.2 feed the same register to every v_dot2c.
@@ -316,34 +290,43 @@ __global__ __launch_bounds__(NW * 64) void win_attn_bf16_kernel(const uint16_t* 
                                                   __builtin_bit_cast(bf16x2_t, 0x3f803f80u), lsum, false);
             packed[e] = w;
           }
-          pf[qb][kb * 2 + ch] = __builtin_bit_cast(bf16x8_t, packed);
+          pf[kb * 2 + ch] = __builtin_bit_cast(bf16x8_t, packed);
         }
       }
-      l_run[qb] += lsum;
+      l_run += lsum;
     }
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T; the 16 keys of chunk (kb, ch) are rows 32kb + 16ch + 8hh + 0..7
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(&Vt[v_frag_off[db] + 32 * kb + 16 * ch]);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][kb * 2 + ch], oacc[qb][db], 0, 0, 0);
+          const char* a0 = vs + v_rd + ((32 * kb + 16 * ch) / RPG) * RG + 2 * db * CS;
+          const char* a1 = vs + v_rd + ((32 * kb + 16 * ch + 4) / RPG) * RG + ((32 * kb + 16 * ch + 4) % RPG) * 16 -
+                           ((32 * kb + 16 * ch) % RPG) * 16 + 2 * db * CS;
+          const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)a0);
+          const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)a1);
+          const bf16x8_t vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb * 2 + ch], oacc[db], 0, 0, 0);
         }
       }
     }
+    __syncthreads();  // next tile resident; everyone is done with this stage
+  };
+
+  __syncthreads();  // tile 0 resident
+  for (int t = 0; t < p.kv_tiles; t += 2) {
+    tile_step(t, stage0, stage1);
+    if (t + 1 < p.kv_tiles) tile_step(t + 1, stage1, stage0);
   }
 
   // ---- normalise and store each row at its original (un-shifted) position
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l = wave_half_sum(l_run[qb]);
+  {
+    const float l = wave_half_sum(l_run);
     const float inv = 1.0f / l;
-    const int row = tile.qtile * BM + (wave * QB + qb) * 32 + l32;
+    const int row = tile.qtile * BM + wave * 32 + l32;
     if (row < p.wtok) {
       const int tok = token_of(p.map, org, uint32_t(row));
       u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + base + int64_t(tok) * D + hh * (D / 2));
@@ -354,7 +337,7 @@ __global__ __launch_bounds__(NW * 64) void win_attn_bf16_kernel(const uint16_t* 
           u32x4_t w;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            w[e] = pack_bf16x2(oacc[qb][db][8 * half + 2 * e] * inv, oacc[qb][db][8 * half + 2 * e + 1] * inv);
+            w[e] = pack_bf16x2(oacc[db][8 * half + 2 * e] * inv, oacc[db][8 * half + 2 * e + 1] * inv);
           dst[db * 2 + half] = w;
         }
       }
@@ -466,15 +449,15 @@ __global__ void win_perm_kernel(WinMap map, int32_t wtok, int32_t total, int32_t
 }
 
 // ---------------------------------------------------------------------------------
-template <int D, int NW, int QB>
+template <int D, int NW>
 static hipError_t launch_bf16(const void* q, const void* k, const void* v, void* out, AttnParams p,
                               hipStream_t stream) {
-  using C = Bf16Cfg<D, NW, QB>;
+  using C = Bf16Cfg<D, NW>;
   p.q_tiles = (p.wtok + C::BM - 1) / C::BM;
   p.kv_tiles = (p.wtok + C::BN - 1) / C::BN;
   const uint64_t blocks = uint64_t(p.q_tiles) * uint64_t(p.n_win) * uint64_t(p.heads_total);
   if (blocks == 0 || blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((win_attn_bf16_kernel<D, NW, QB>), dim3(uint32_t(blocks)), dim3(C::NT), 0, stream,
+  hipLaunchKernelGGL((win_attn_bf16_kernel<D, NW>), dim3(uint32_t(blocks)), dim3(C::NT), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), p);
   return hipGetLastError();
@@ -496,8 +479,8 @@ static hipError_t launch_f32(const void* q, const void* k, const void* v, void* 
 hipError_t launch_window_attention(const void* q, const void* k, const void* v, void* out, const AttnParams& p,
                                    int head_dim, bool bf16, hipStream_t stream) {
   if (bf16) {
-    if (head_dim == 128) return launch_bf16<128, 4, 1>(q, k, v, out, p, stream);
-    if (head_dim == 64) return launch_bf16<64, 4, 1>(q, k, v, out, p, stream);
+    if (head_dim == 128) return launch_bf16<128, 8>(q, k, v, out, p, stream);
+    if (head_dim == 64) return launch_bf16<64, 8>(q, k, v, out, p, stream);
   } else {
     if (head_dim == 128) return launch_f32<128>(q, k, v, out, p, stream);
     if (head_dim == 64) return launch_f32<64>(q, k, v, out, p, stream);
