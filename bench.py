@@ -13,7 +13,6 @@ Prints ONE JSON line (rank 0). Usage:
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -22,7 +21,9 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from sparse_attention_dit_amd.configs import BY_NAME, WORKLOADS  # noqa: E402
+from sparse_attention_dit_amd.build import kernel_hash  # noqa: E402
+from sparse_attention_dit_amd.configs import BY_NAME  # noqa: E402
+from sparse_attention_dit_amd.profiling import traffic_json_name  # noqa: E402
 
 # MI355X published peaks: dense bf16 MFMA 2.5 PFLOP/s (256 CU x 2.4 GHz x 4096 flop/clk),
 # fp32 vector 157.3 TFLOP/s, HBM3E 8 TB/s.
@@ -30,22 +31,12 @@ PEAK_BF16_TFLOPS = 2516.6
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "flux-2048-128x128-w32"
-KERNEL_SOURCES = ("sparse_attention_dit_amd/csrc/attn_kernels.hip", "sparse_attention_dit_amd/csrc/index_map.hpp",
-                  "sparse_attention_dit_amd/csrc/attn_launch.hpp")
-
-
-def kernel_hash() -> str:
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary of this
     workload, if it was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    path = os.path.join(ROOT, "profiles", traffic_json_name(workload))
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -55,10 +46,10 @@ def measured_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s: float):
+def cpu_baseline(w, min_s: float):
     """Time the fp64 oracle (as it stands) on a bounded sample of the workload: whole
-    heads of the windowed attention for one shift, until ~budget_s of CPU work."""
-    import numpy as np
+    (shift, head) slices of the windowed attention, in step order and cycling, until at
+    least min_s of CPU work."""
     from oracle import basa_oracle as O
     from sparse_attention_dit_amd import inputs
     try:
@@ -68,19 +59,20 @@ def cpu_baseline(w, budget_s: float):
         threads = None
     t = inputs.draw_qkv((w.batch, 1, w.tokens, w.head_dim), w.dtype, seed=w.seed)
     q, k, v = (t.exact[n] for n in "qkv")
-    heads_done, elapsed = 0, 0.0
-    while heads_done < w.heads and elapsed < budget_s:
+    slices, elapsed = 0, 0.0
+    while elapsed < min_s:
         t0 = time.perf_counter()
-        O.window_attention(q, k, v, w.grid, w.window, w.shifts[0])
+        O.window_attention(q, k, v, w.grid, w.window, w.shifts[(slices // w.heads) % len(w.shifts)])
         elapsed += time.perf_counter() - t0
-        heads_done += 1
-    flops = 4 * w.batch * heads_done * w.tokens * w.window_tokens * w.head_dim
+        slices += 1
+    flops = 4 * w.batch * slices * w.tokens * w.window_tokens * w.head_dim
     return {
         "value": flops / elapsed / 1e12,
         "unit": "TFLOP/s",
         "cores": threads if threads is not None else len(os.sched_getaffinity(0)),
         "kind": "oracle",
-        "sample": f"{heads_done} of {w.heads} heads x {w.num_windows} windows, shift {w.shifts[0]}, fp64 numpy "
+        "sample": f"{slices} (shift, head) slices of {w.num_windows} windows each (one step = "
+                  f"{len(w.shifts) * w.heads}), fp64 numpy, one head's q/k/v drawn with the workload seed "
                   f"({flops / 1e9:.1f} GFLOP in {elapsed:.1f} s)",
     }
 
@@ -93,7 +85,7 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(BY_NAME))
     ap.add_argument("--full-iters", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline leg")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU work timed for cpu_baseline")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -182,7 +174,7 @@ def main():
         "kernel_hash": kernel_hash(),
     }
     if not args.no_cpu:
-        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
 
 

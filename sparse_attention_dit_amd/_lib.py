@@ -10,7 +10,8 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libbasa.so")
+# BASA_LIB may name another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("BASA_LIB") or os.path.join(_PKG, "libbasa.so")
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1

@@ -5,6 +5,7 @@ hipcc cross-compiles for gfx950 without a GPU present.
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -14,11 +15,23 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbasa.so")
 SOURCES = ("basa_abi.cpp", "attn_kernels.hip")
+# files whose contents decide the kernels' machine code (the attention and index kernels)
+KERNEL_SOURCES = ("attn_kernels.hip", "index_map.hpp", "attn_launch.hpp")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are disabled for every device pass.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def kernel_hash() -> str:
+    """Short digest of the kernel sources: counter summaries record it, so a summary taken
+    on other kernel code is recognised as stale."""
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(CSRC, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def build(verbose: bool = False) -> str:

@@ -130,7 +130,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void win_attn_bf16_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void win_attn_bf16_kernel(const uint16_t* __restrict__ q,
                                                                     const uint16_t* __restrict__ k,
                                                                     const uint16_t* __restrict__ v,
                                                                     uint16_t* __restrict__ out,
@@ -231,15 +231,18 @@ __global__ __launch_bounds__(NW * 64, 1) void win_attn_bf16_kernel(const uint16_
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+    bf16x8_t kf[DK][2];
 #pragma unroll
-    for (int kk = 0; kk < DK; ++kk) {
+    for (int kk = 0; kk < DK; ++kk)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8_t kf =
-            *reinterpret_cast<const bf16x8_t*>(ks + k_rd + kb * (32 / RPG) * RG + kk * CS);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[kb], 0, 0, 0);
-      }
-    }
+      for (int kb = 0; kb < 2; ++kb)
+        kf[kk][kb] = *reinterpret_cast<const bf16x8_t*>(ks + k_rd + kb * (32 / RPG) * RG + kk * CS);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk][kb], qf[kk], sacc[kb], 0, 0, 0);
 
     // ragged last tile: keys past the window get -inf
     if ((t + 1) * BN > p.wtok) {

@@ -1,0 +1,84 @@
+"""Host logic of the profile summaries: counter scaling and launch splitting, on small
+hand-made CSV files shaped like rocprofv3's output."""
+import csv
+import json
+import os
+
+import pytest
+
+from sparse_attention_dit_amd import profiling
+from sparse_attention_dit_amd.build import kernel_hash
+from sparse_attention_dit_amd.configs import BY_NAME
+
+COUNTER_COLS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id", "Grid_Size",
+                "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size", "VGPR_Count",
+                "Accum_VGPR_Count", "SGPR_Count", "Counter_Name", "Counter_Value", "Start_Timestamp",
+                "End_Timestamp"]
+
+
+def _counters(path, rows):
+    os.makedirs(path)
+    with open(os.path.join(path, "x_counter_collection.csv"), "w", newline="") as f:
+        wr = csv.DictWriter(f, COUNTER_COLS)
+        wr.writeheader()
+        for i, (kernel, counter, value) in enumerate(rows):
+            r = dict.fromkeys(COUNTER_COLS, "0")
+            r.update(Dispatch_Id=str(i + 1), Kernel_Name=kernel, Counter_Name=counter, Counter_Value=str(value))
+            wr.writerow(r)
+
+
+def test_traffic_scaling(tmp_path):
+    k = "void basa::win_attn_bf16_kernel<128, 8>(...)"
+    c = "__amd_rocclr_copyBuffer"
+    _counters(tmp_path / "f", [(k, "FETCH_SIZE", 100.0), (k, "FETCH_SIZE", 102.0), ("other", "FETCH_SIZE", 1e9)])
+    _counters(tmp_path / "w", [(k, "WRITE_SIZE", 50.0)])
+    half = profiling.COPY_BYTES / 1024 / 2
+    _counters(tmp_path / "cf", [(c, "FETCH_SIZE", half)])                  # counter reads half the bytes
+    _counters(tmp_path / "cw", [(c, "WRITE_SIZE", profiling.COPY_BYTES / 1024)])
+    out = tmp_path / "out"
+    wl = "flux-2048-128x128-w32"
+    profiling.main(["traffic", "--fetch", str(tmp_path / "f"), "--write", str(tmp_path / "w"),
+                    "--copy-fetch", str(tmp_path / "cf"), "--copy-write", str(tmp_path / "cw"),
+                    "--workload", wl, "--cmd", "cmd", "--out-dir", str(out)])
+    rec = json.load(open(out / profiling.traffic_json_name(wl)))
+    assert rec["fetch_bytes_per_launch"] == round(101.0 * 1024 * 2)
+    assert rec["write_bytes_per_launch"] == 50 * 1024
+    assert rec["hbm_bytes_per_launch"] == rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    assert rec["algorithmic_bytes_per_launch"] == BY_NAME[wl].io_bytes()
+    assert rec["kernel_hash"] == kernel_hash()
+
+
+def test_kernel_stats_split(tmp_path):
+    d = tmp_path / "t"
+    os.makedirs(d)
+    cols = ["Kind", "Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+    with open(d / "b_kernel_trace.csv", "w", newline="") as f:
+        wr = csv.DictWriter(f, cols)
+        wr.writeheader()
+        rows = [(3, 1000), (1, 2000), (2, 4000), (5, 30000), (4, 50000)]   # (dispatch, ns), unordered
+        for did, ns in rows:
+            wr.writerow({"Kind": "KERNEL_DISPATCH", "Dispatch_Id": did,
+                         "Kernel_Name": "void basa::win_attn_bf16_kernel<128, 8>(x)",
+                         "Start_Timestamp": 10, "End_Timestamp": 10 + ns})
+        wr.writerow({"Kind": "KERNEL_DISPATCH", "Dispatch_Id": 6, "Kernel_Name": "other",
+                     "Start_Timestamp": 0, "End_Timestamp": 10 ** 9})
+    out = tmp_path / "s.md"
+    profiling.main(["kernel-stats", "--dir", str(d), "--windowed", "3", "--cmd", "c", "--out", str(out)])
+    text = out.read_text()
+    # dispatches 1..3 are the windowed launches (2000, 1000, 4000 ns), 4..5 the dense ones
+    assert "| windowed (bench steps, incl. warm-up) | 3 | 2.33 | 2.00 | 1.00 | 4.00 |" in text
+    assert "| dense baseline | 2 | 40.00 | 40.00 | 30.00 | 50.00 |" in text
+
+
+def test_committed_traffic_records_are_consistent():
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    pdir = os.path.join(root, "profiles")
+    found = [f for f in os.listdir(pdir) if f.endswith(".traffic.json")] if os.path.isdir(pdir) else []
+    if not found:
+        pytest.skip("no committed traffic record")
+    for name in found:
+        rec = json.load(open(os.path.join(pdir, name)))
+        wl = BY_NAME[rec["workload"]]
+        assert name == profiling.traffic_json_name(wl.name)
+        assert rec["algorithmic_bytes_per_launch"] == wl.io_bytes()
+        assert rec["hbm_bytes_per_launch"] == rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
