@@ -45,7 +45,9 @@ typedef enum {
   BASA_ERR_SHAPE = 2,       /* non-positive size, or window does not divide the grid */
   BASA_ERR_UNSUPPORTED = 3, /* dtype or head_dim outside the supported set */
   BASA_ERR_ALIAS = 4,       /* out overlaps q, k or v */
-  BASA_ERR_OVERFLOW = 5,    /* a size or index does not fit the 32-bit per-head indexing */
+  BASA_ERR_OVERFLOW = 5,    /* a size or index does not fit the 32-bit per-head indexing:
+                               T*H*W, B*heads and N*head_dim must not exceed 2^31-1, and
+                               for bf16 one head must not exceed 0xffffff00 bytes */
   BASA_ERR_HIP = 6,         /* the HIP runtime rejected the launch (hipGetLastError) */
   BASA_ERR_ALIGN = 7        /* a tensor pointer is not 16-byte aligned */
 } basa_status;

@@ -13,6 +13,7 @@
 namespace {
 
 constexpr int64_t kInt32Max = 0x7fffffff;
+constexpr uint32_t kBf16HeadBytesMax = 0xffffff00u;
 
 int reduce_mod(int s, int n) {
   const int r = s % n;  // in (-n, n)
@@ -44,6 +45,10 @@ int run_attention(const void* q, const void* k, const void* v, void* out, int B,
   const int64_t N = int64_t(T) * H * W;
   const int64_t bh = int64_t(B) * heads;
   if (bh > kInt32Max || N * head_dim > kInt32Max) return BASA_ERR_OVERFLOW;
+  // The bf16 kernel addresses one head through a buffer resource of 32-bit byte range and
+  // reads rows past a window at byte offsets from 0xffffff00 up, which must lie outside the
+  // head's range to read as zeros.
+  if (dtype == BASA_DTYPE_BF16 && N * head_dim * 2 > int64_t(kBf16HeadBytesMax)) return BASA_ERR_OVERFLOW;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return BASA_ERR_ALIGN;
   const int64_t elem = dtype == BASA_DTYPE_BF16 ? 2 : 4;
   const int64_t bytes = bh * N * head_dim * elem;

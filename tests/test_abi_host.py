@@ -70,6 +70,8 @@ def _win(q=A, k=Bp, v=Cp, out=D, B=1, heads=2, grid=(1, 16, 16), window=(1, 8, 8
     (dict(grid=(1, 65536, 65536), window=(1, 1, 1)), 5),
     (dict(grid=(1, 4096, 8192), window=(1, 1, 1), head_dim=128), 5),
     (dict(B=65536, heads=65536), 5),
+    # bf16: one head may hold at most 0xffffff00 bytes (N*d = 0x7fffffc0 here: 0xffffff80 bytes)
+    (dict(grid=(1, 1, 0x7fffffc0 // 64), window=(1, 1, 1), dtype=1), 5),
     (dict(q=A + 8), 7), (dict(out=D + 4), 7),
 ])
 def test_argument_errors_return_codes(kw, code):
