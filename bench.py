@@ -8,7 +8,7 @@ protocol (§4 / App. A.2 "Implementation and latency measurement"): warm-up firs
 events around the timed region, synchronisation before reading them.
 
 Prints ONE JSON line (rank 0). Usage:
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--cold]
 """
 from __future__ import annotations
 
@@ -82,9 +82,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-s", type=float, default=0.5, help="seconds of untimed steps before the warm-up")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(BY_NAME))
     ap.add_argument("--full-iters", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline leg")
+    ap.add_argument("--cold", action="store_true", help="also time HBM-cold launches (L2/MALL flushed between)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU work timed for cpu_baseline")
     args = ap.parse_args()
 
@@ -114,6 +116,19 @@ def main():
         for s in w.shifts:
             _lib.window_attn_fwd(dev["q"], dev["k"], dev["v"], out, w.grid, w.window, s, stream)
 
+    # The GPU's clocks need tens of milliseconds of sustained work to ramp up: before the W
+    # warm-up steps, run untimed steps for ~0.5 s (sized from one step), reported as
+    # "clock_settle_steps".
+    settle = 0
+    if args.settle_s > 0:
+        step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        step()
+        torch.cuda.synchronize()
+        settle = 2 + int(args.settle_s / max(time.perf_counter() - t0, 1e-6))
+        for _ in range(settle - 2):
+            step()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -127,6 +142,38 @@ def main():
     ms_per_step = ms_total / args.steps
     launches = args.steps * len(w.shifts)
     ms_per_launch = ms_total / launches
+
+    # each shift of the cycle on its own (same launches, timed per shift)
+    per_shift_ms = []
+    for s in w.shifts:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            _lib.window_attn_fwd(dev["q"], dev["k"], dev["v"], out, w.grid, w.window, s, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per_shift_ms.append(round(e0.elapsed_time(e1) / args.steps, 4))
+
+    cold = None
+    if args.cold:
+        # HBM-cold launches: a 1 GiB write between launches (outside the events) evicts
+        # q/k/v from the L2s and the MALL; median over the launches
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        times = []
+        for i in range(args.steps):
+            flush.fill_(i & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            _lib.window_attn_fwd(dev["q"], dev["k"], dev["v"], out, w.grid, w.window, w.shifts[i % len(w.shifts)],
+                                 stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        del flush
+        med = sorted(times)[len(times) // 2]
+        cold = {"window_attn_ms_median": round(med, 4),
+                "tflops": round(w.window_flops() / (med * 1e-3) / 1e12, 2),
+                "io_gbs": round(w.io_bytes() / (med * 1e-3) / 1e9, 1)}
 
     # dense baseline: same kernel, window = whole grid
     full_out = torch.empty_like(dev["q"])
@@ -155,6 +202,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle_steps": settle,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -170,9 +218,12 @@ def main():
                     "measured": round(measured, 3), "theoretical": theoretical,
                     "ratio": round(measured / theoretical, 4),
                     "full_attn_tflops": round(w.full_flops() / (ms_full * 1e-3) / 1e12, 2)},
+        "per_shift_ms": per_shift_ms,
         "io_gbs": round(io_gbs, 1),
         "kernel_hash": kernel_hash(),
     }
+    if cold is not None:
+        rec["cold"] = cold
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

@@ -6,8 +6,8 @@ plain device-to-device copy of known size, a fixed number of times.
 
 ``kernel-stats``: turns the CSV of a ``rocprofv3 --kernel-trace --stats`` run of bench.py
 into a markdown summary: per-launch durations of the attention kernel, split into the
-windowed launches and the dense baseline launches by their order (bench.py issues all
-windowed launches first).
+windowed launches and the dense baseline launches by their order (bench.py makes the
+dense launches last: 2 untimed + --full-iters timed).
 
 ``traffic``: turns four ``rocprofv3 --pmc`` passes (FETCH_SIZE and WRITE_SIZE over the
 windowed kernel, the same two over the copy) into HBM bytes per launch. Each counter is
@@ -17,7 +17,7 @@ keyed by the kernel-source digest) and a markdown summary beside it.
 
 Usage (inside the profiler, then on the CSV it wrote):
   python3 -m sparse_attention_dit_amd.profiling run --what window --workload NAME --iters 4
-  python3 -m sparse_attention_dit_amd.profiling kernel-stats --dir D --windowed N --cmd "..." --out F
+  python3 -m sparse_attention_dit_amd.profiling kernel-stats --dir D --dense 7 --cmd "..." --out F
   python3 -m sparse_attention_dit_amd.profiling traffic --fetch D1 --write D2 --copy-fetch D3 \\
       --copy-write D4 --workload NAME --cmd "..." --out-dir profiles
 """
@@ -119,25 +119,31 @@ def _stats_table(durations_ns):
 
 
 # ------------------------------------------------------------------ summaries
-def _kernel_stats(directory: str, windowed: int, cmd: str, out: str, bench_json: str | None) -> None:
+def _kernel_stats(directory: str, dense: int, cmd: str, out: str, bench_json: str | None) -> None:
     rows = _kernel_rows(directory)
-    if len(rows) <= windowed:
-        raise ValueError(f"{len(rows)} attention dispatches, expected more than {windowed}")
+    if len(rows) <= dense:
+        raise ValueError(f"{len(rows)} attention dispatches, expected more than {dense}")
     dur = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows]
-    win, full = _stats_table(dur[:windowed]), _stats_table(dur[windowed:])
+    win, full = _stats_table(dur[:-dense]), _stats_table(dur[-dense:])
     name = rows[0]["Kernel_Name"]
     lines = [f"# Kernel trace: {ATTN_KERNEL}", "", "Command (from the repository root):", "", "```", cmd, "```", "",
              f"Kernel: `{name[:120]}`", "",
              "| launches | calls | avg µs | median µs | min µs | max µs |", "|---|---|---|---|---|---|"]
-    for label, s in (("windowed (bench steps, incl. warm-up)", win), ("dense baseline", full)):
+    for label, s in (("windowed (all of bench.py's windowed launches)", win), ("dense baseline", full)):
         lines.append(f"| {label} | {s['calls']} | {s['avg_us']:.2f} | {s['median_us']:.2f} | {s['min_us']:.2f} | "
                      f"{s['max_us']:.2f} |")
     if bench_json:
         with open(bench_json) as f:
             b = json.loads(f.read().strip().splitlines()[-1])
+        # bench.py's windowed launches, in order: clock settle, warm-up, the timed steps, ...
+        per_step = len(b["config"]["shifts"])
+        first = (b["clock_settle_steps"] + b["warmup"]) * per_step
+        timed = _stats_table(dur[first:first + b["steps"] * per_step])
+        lines.append(f"| windowed, bench.py's timed steps only | {timed['calls']} | {timed['avg_us']:.2f} | "
+                     f"{timed['median_us']:.2f} | {timed['min_us']:.2f} | {timed['max_us']:.2f} |")
         lines += ["", "bench.py's own line for the same run (HIP events around the timed steps):", "",
                   f"- windowed: {b['speedup']['window_attn_ms'] * 1e3:.2f} µs per launch "
-                  f"({b['value']} TFLOP/s)",
+                  f"({b['value']} TFLOP/s); rocprofv3 average over the same launches: {timed['avg_us']:.2f} µs",
                   f"- dense: {b['speedup']['full_attn_ms'] * 1e3:.2f} µs per launch"]
     stats_csv = glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True)
     if stats_csv:
@@ -216,7 +222,7 @@ def main(argv=None) -> None:
     r.add_argument("--iters", type=int, default=4)
     k = sub.add_parser("kernel-stats")
     k.add_argument("--dir", required=True)
-    k.add_argument("--windowed", type=int, required=True, help="number of windowed launches bench.py made")
+    k.add_argument("--dense", type=int, default=7, help="number of trailing dense launches bench.py made")
     k.add_argument("--cmd", required=True)
     k.add_argument("--out", required=True)
     k.add_argument("--bench-json", default=None)
@@ -231,7 +237,7 @@ def main(argv=None) -> None:
     if a.cmd_name == "run":
         _run(a.what, a.workload, a.iters)
     elif a.cmd_name == "kernel-stats":
-        _kernel_stats(a.dir, a.windowed, a.cmd, a.out, a.bench_json)
+        _kernel_stats(a.dir, a.dense, a.cmd, a.out, a.bench_json)
     else:
         _traffic(a)
 

@@ -63,10 +63,10 @@ def test_kernel_stats_split(tmp_path):
         wr.writerow({"Kind": "KERNEL_DISPATCH", "Dispatch_Id": 6, "Kernel_Name": "other",
                      "Start_Timestamp": 0, "End_Timestamp": 10 ** 9})
     out = tmp_path / "s.md"
-    profiling.main(["kernel-stats", "--dir", str(d), "--windowed", "3", "--cmd", "c", "--out", str(out)])
+    profiling.main(["kernel-stats", "--dir", str(d), "--dense", "2", "--cmd", "c", "--out", str(out)])
     text = out.read_text()
     # dispatches 1..3 are the windowed launches (2000, 1000, 4000 ns), 4..5 the dense ones
-    assert "| windowed (bench steps, incl. warm-up) | 3 | 2.33 | 2.00 | 1.00 | 4.00 |" in text
+    assert "| windowed (all of bench.py's windowed launches) | 3 | 2.33 | 2.00 | 1.00 | 4.00 |" in text
     assert "| dense baseline | 2 | 40.00 | 40.00 | 30.00 | 50.00 |" in text
 
 
