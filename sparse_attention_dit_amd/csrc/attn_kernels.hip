@@ -165,20 +165,46 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int ld_row = lane % RPG;
   const uint32_t k_chunk_off = uint32_t(ld_slot) * 16u;
   const uint32_t v_chunk_off = uint32_t(L::v_slot(ld_slot)) * 16u;
-  auto issue_tile = [&](int t, char* st) {
+  // Byte offset of a window row in the head (rows past the window get an offset beyond the
+  // buffer range, so they read as zeros).
+  auto row_offset = [&](int local) __attribute__((always_inline)) -> uint32_t {
+    return local < p.wtok ? uint32_t(token_of(p.map, org, uint32_t(local))) * uint32_t(L::ROW_BYTES) : 0xffffff00u;
+  };
+  auto dma_tile = [&](const uint32_t* row_off, char* st) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int g = wave * C::LOADS + i;
-      const int local = t * BN + g * RPG + ld_row;
-      uint32_t row_off = 0xffffff00u;  // rows past the window read as zeros
-      if (local < p.wtok) row_off = uint32_t(token_of(p.map, org, uint32_t(local))) * uint32_t(L::ROW_BYTES);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void_t*)(st + g * RG), 16, row_off + k_chunk_off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void_t*)(st + g * RG), 16, row_off[i] + k_chunk_off, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_t*)(st + C::TILE_BYTES + g * RG), 16,
-                                               row_off + v_chunk_off, 0, 0, 0);
+                                               row_off[i] + v_chunk_off, 0, 0, 0);
     }
   };
+  // The row offsets of the K/V tiles are computed cooperatively a few tiles ahead into a
+  // ring of TAB_TILES tiles in LDS (one row per thread per refill), and each lane reads the
+  // LOADS offsets it needs one step before it issues the DMA. The shift/partition index
+  // arithmetic thus costs a few instructions per 8 tiles instead of several per row.
+  constexpr int TAB_TILES = 16;
+  constexpr int REFILL = 8;  // tiles per refill
+  __shared__ uint32_t rowtab[TAB_TILES * BN];
+  auto fill_tab = [&](int first, int ntiles) __attribute__((always_inline)) {
+    for (int e = tid; e < ntiles * BN; e += C::NT) {
+      const int t = first + e / BN;
+      rowtab[(t % TAB_TILES) * BN + e % BN] = row_offset(t * BN + e % BN);
+    }
+  };
+  auto read_offs = [&](int t, uint32_t* row_off) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i)
+      row_off[i] = rowtab[(t % TAB_TILES) * BN + (wave * C::LOADS + i) * RPG + ld_row];
+  };
 
-  issue_tile(0, stage0);
+  {  // tile 0 straight from the index map, the table for tiles 0 .. TAB_TILES - 1
+    uint32_t off0[C::LOADS];
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) off0[i] = row_offset((wave * C::LOADS + i) * RPG + ld_row);
+    dma_tile(off0, stage0);
+  }
+  fill_tab(0, min(TAB_TILES, p.kv_tiles));
 
   // ---- Q fragments (B operand of S^T): lane holds d = hh*D/2 + 8*kk .. +7 of its row.
   bf16x8_t qf[DK];
@@ -219,9 +245,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   float m_run = -__builtin_inff(), l_run = 0.0f;
   const float c = p.scale_log2;
 
-  // One K/V tile: prefetch tile t+1 into `nxt`, compute tile t from `cur`.
+  // One K/V tile: prefetch tile t+1 into `nxt`, compute tile t from `cur`. `next_off`
+  // holds the row offsets of tile t+1 (read from the table during the previous step).
+  uint32_t next_off[C::LOADS];
   auto tile_step = [&](int t, const char* cur, char* nxt) {
-    if (t + 1 < p.kv_tiles) issue_tile(t + 1, nxt);
+    if (t + 1 < p.kv_tiles) dma_tile(next_off, nxt);
+    if (t + 2 < p.kv_tiles) read_offs(t + 2, next_off);
+    // refill the ring slots of tiles t-8 .. t-1 (all issued) with tiles t+8 .. t+15, first
+    // needed by the DMA of step t+7; the barrier ending this step publishes them
+    if (t % REFILL == 0 && t >= REFILL && t + REFILL < p.kv_tiles)
+      fill_tab(t + REFILL, min(REFILL, p.kv_tiles - t - REFILL));
     const char* ks = cur;
     const char* vs = cur + C::TILE_BYTES;
 
@@ -319,7 +352,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     __syncthreads();  // next tile resident; everyone is done with this stage
   };
 
-  __syncthreads();  // tile 0 resident
+  __syncthreads();  // tile 0 resident, row table written
+  if (1 < p.kv_tiles) read_offs(1, next_off);
   for (int t = 0; t < p.kv_tiles; t += 2) {
     tile_step(t, stage0, stage1);
     if (t + 1 < p.kv_tiles) tile_step(t + 1, stage1, stage0);
@@ -333,17 +367,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (row < p.wtok) {
       const int tok = token_of(p.map, org, uint32_t(row));
       u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + base + int64_t(tok) * D + hh * (D / 2));
+      // All words are packed (into the low half of each O block) before the first store:
+      // a store reads its data registers late, and rewriting them for the next chunk
+      // would make every store wait for the one before it.
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          oacc[db][i] = __uint_as_float(pack_bf16x2(oacc[db][2 * i] * inv, oacc[db][2 * i + 1] * inv));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           u32x4_t w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            w[e] = pack_bf16x2(oacc[db][8 * half + 2 * e] * inv, oacc[db][8 * half + 2 * e + 1] * inv);
+          for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(oacc[db][4 * half + e]);
           dst[db * 2 + half] = w;
         }
-      }
     }
   }
 }
