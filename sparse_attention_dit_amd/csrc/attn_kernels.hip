@@ -129,6 +129,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Device-only builtins are called through __device__ functions: called directly from a
+// lambda inside a kernel template, the buffer-to-LDS builtin can make hipcc's host pass
+// drop the kernel's launch stub without a diagnostic.
+__device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t rs, char* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)dst, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t rs, uint32_t off, u32x4_t x) {
+  __builtin_amdgcn_raw_buffer_store_b128(x, rs, off, 0, 0);
+}
+
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void win_attn_bf16_kernel(const uint16_t* __restrict__ q,
                                                                     const uint16_t* __restrict__ k,
@@ -174,9 +184,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int g = wave * C::LOADS + i;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void_t*)(st + g * RG), 16, row_off[i] + k_chunk_off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_t*)(st + C::TILE_BYTES + g * RG), 16,
-                                               row_off[i] + v_chunk_off, 0, 0, 0);
+      dma16_to_lds(krs, st + g * RG, row_off[i] + k_chunk_off);
+      dma16_to_lds(vrs, st + C::TILE_BYTES + g * RG, row_off[i] + v_chunk_off);
     }
   };
   // The row offsets of the K/V tiles are computed cooperatively a few tiles ahead into a
@@ -206,20 +215,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
   fill_tab(0, min(TAB_TILES, p.kv_tiles));
 
-  // ---- Q fragments (B operand of S^T): lane holds d = hh*D/2 + 8*kk .. +7 of its row.
-  bf16x8_t qf[DK];
+  // ---- Q: each wave DMAs its own 32 rows into the Q buffer (laid out like a K tile, 4 whole
+  // rows per wave-wide load), and after the prologue barrier reads its fragments from there.
+  // qrowtab keeps the byte offset of every query row for the output stores.
+  constexpr int QG = 32 / RPG;  // row groups per wave
+  __shared__ __attribute__((aligned(1024))) char qbuf[NW * QG * RG];
+  __shared__ uint32_t qrowtab[BM];
   {
-    const int row = tile.qtile * BM + wave * 32 + l32;
-    if (row < p.wtok) {
-      const int tok = token_of(p.map, org, uint32_t(row));
-      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(q + base + int64_t(tok) * D + hh * (D / 2));
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q + base, head_bytes);
 #pragma unroll
-      for (int kk = 0; kk < DK; ++kk) qf[kk] = __builtin_bit_cast(bf16x8_t, src[kk]);
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < DK; ++kk) qf[kk] = __builtin_bit_cast(bf16x8_t, u32x4_t{0, 0, 0, 0});
+    for (int i = 0; i < QG; ++i) {
+      const int g = wave * QG + i;
+      dma16_to_lds(qrs, qbuf + g * RG, row_offset(tile.qtile * BM + g * RPG + ld_row) + k_chunk_off);
     }
+    if (tid < BM) qrowtab[tid] = row_offset(tile.qtile * BM + tid);
   }
+  // B operand of S^T: lane holds d = hh*D/2 + 8*kk .. +7 of query row wave*32 + l32
+  const int qrow = wave * 32 + l32;
+  const int q_rd = (qrow / RPG) * RG + (qrow % RPG) * 16 + hh * (CPR / 2) * CS;
+  bf16x8_t qf[DK];
 
   // ---- per-lane LDS read bases (all per-step offsets below are compile-time constants)
   // K (A operand of S^T): row 32*kb + key_perm(l32), chunk hh*CPR/2 + kk.
@@ -352,40 +366,40 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     __syncthreads();  // next tile resident; everyone is done with this stage
   };
 
-  __syncthreads();  // tile 0 resident, row table written
+  __syncthreads();  // tile 0 and Q resident, row tables written
+#pragma unroll
+  for (int kk = 0; kk < DK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qbuf + q_rd + kk * CS);
   if (1 < p.kv_tiles) read_offs(1, next_off);
   for (int t = 0; t < p.kv_tiles; t += 2) {
     tile_step(t, stage0, stage1);
     if (t + 1 < p.kv_tiles) tile_step(t + 1, stage1, stage0);
   }
 
-  // ---- normalise and store each row at its original (un-shifted) position
+  // ---- normalise and store each row at its original (un-shifted) position. The packed rows
+  // go through this wave's part of the Q buffer, so that each wave-wide store writes RPG
+  // whole rows (16 lanes per 256-byte row) instead of 16 bytes of 64 different rows.
   {
     const float l = wave_half_sum(l_run);
     const float inv = 1.0f / l;
-    const int row = tile.qtile * BM + wave * 32 + l32;
-    if (row < p.wtok) {
-      const int tok = token_of(p.map, org, uint32_t(row));
-      u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + base + int64_t(tok) * D + hh * (D / 2));
-      // All words are packed (into the low half of each O block) before the first store:
-      // a store reads its data registers late, and rewriting them for the next chunk
-      // would make every store wait for the one before it.
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          oacc[db][i] = __uint_as_float(pack_bf16x2(oacc[db][2 * i] * inv, oacc[db][2 * i + 1] * inv));
-      __builtin_amdgcn_sched_barrier(0);
+      for (int half = 0; half < 2; ++half) {
+        u32x4_t w;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+        for (int e = 0; e < 4; ++e)
+          w[e] = pack_bf16x2(oacc[db][8 * half + 2 * e] * inv, oacc[db][8 * half + 2 * e + 1] * inv);
+        // chunk hh*CPR/2 + 2*db + half of row qrow
+        *reinterpret_cast<u32x4_t*>(qbuf + q_rd + (2 * db + half) * CS) = w;
+      }
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(out + base, head_bytes);
+    u32x4_t w[QG];
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          u32x4_t w;
+    for (int i = 0; i < QG; ++i)
+      w[i] = *reinterpret_cast<const u32x4_t*>(qbuf + (wave * QG + i) * RG + ld_slot * CS + ld_row * 16);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(oacc[db][4 * half + e]);
-          dst[db * 2 + half] = w;
-        }
-    }
+    for (int i = 0; i < QG; ++i)
+      buffer_store16(ors, qrowtab[(wave * QG + i) * RPG + ld_row] + k_chunk_off, w[i]);
   }
 }
 
