@@ -92,6 +92,20 @@ int basa_full_attn_fwd(const void* q, const void* k, const void* v, void* out,
 int basa_window_perm(int T, int H, int W, int wt, int wh, int ww, int st, int sh, int sw,
                      int32_t* perm, hipStream_t stream);
 
+/*
+ * Interleaved shift schedule (paper §3.1, "Interleaved shift schedule", its three displayed
+ * equations). For L sparse-attention layers and window sides (wh, ww), writes the shift of
+ * layer l at a denoising step with offset (ch, cw) as (dh[l], dw[l]), l = 0 .. L-1:
+ *   per axis, a_i = (i * delta) mod w with delta = max(1, floor(w / L));
+ *   b = (a_0, a_K, a_1, a_{K+1}, ...) with K = ceil(L / 2) (the page prints the even-L
+ *       pattern; for odd L the first half is one longer);
+ *   d[l] = (b_l + c) mod w, c any integer (the page leaves the step offset to the caller).
+ * The result is passed as (sh, sw) to basa_window_attn_fwd, with st = 0: the paper's video
+ * windows keep the whole temporal axis. dh and dw: HOST arrays of L int32, caller-owned.
+ * Host-only: no HIP call. Errors: BASA_ERR_NULL, BASA_ERR_SHAPE (L, wh or ww <= 0).
+ */
+int basa_shift_schedule(int L, int wh, int ww, int ch, int cw, int32_t* dh, int32_t* dw);
+
 /* Static, NUL-terminated description of a basa_status value. Never NULL. */
 const char* basa_status_string(int status);
 

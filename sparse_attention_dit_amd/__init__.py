@@ -8,6 +8,7 @@ from ._lib import (  # noqa: F401
     BasaError,
     full_attn_fwd,
     load,
+    shift_schedule,
     status_string,
     version,
     window_attn_fwd,

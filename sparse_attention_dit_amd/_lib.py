@@ -18,7 +18,7 @@ DTYPE_BF16 = 1
 
 # Exported C symbols, in header order.
 SYMBOLS = ("basa_window_attn_fwd", "basa_full_attn_fwd", "basa_window_perm",
-           "basa_status_string", "basa_version")
+           "basa_shift_schedule", "basa_status_string", "basa_version")
 
 
 class BasaError(RuntimeError):
@@ -45,6 +45,8 @@ def load() -> ctypes.CDLL:
     lib.basa_full_attn_fwd.restype = i
     lib.basa_window_perm.argtypes = [i] * 9 + [vp, vp]
     lib.basa_window_perm.restype = i
+    lib.basa_shift_schedule.argtypes = [i] * 5 + [vp, vp]
+    lib.basa_shift_schedule.restype = i
     lib.basa_status_string.argtypes = [i]
     lib.basa_status_string.restype = ctypes.c_char_p
     lib.basa_version.argtypes = []
@@ -125,6 +127,19 @@ def window_perm(grid, window, shift, perm, stream=None) -> None:
     rc = load().basa_window_perm(T, H, W, wt, wh, ww, st, sh, sw, perm.data_ptr(), _stream_handle(stream))
     if rc != 0:
         raise BasaError(rc, "basa_window_perm")
+
+
+def shift_schedule(L, window_hw, c=(0, 0)):
+    """Per-layer (dh, dw) shifts of the interleaved schedule for a step offset c."""
+    L = int(L)
+    if L <= 0:
+        raise BasaError(2, "L must be positive")
+    dh, dw = (ctypes.c_int32 * L)(), (ctypes.c_int32 * L)()
+    wh, ww = (int(x) for x in window_hw)
+    rc = load().basa_shift_schedule(L, wh, ww, int(c[0]), int(c[1]), dh, dw)
+    if rc != 0:
+        raise BasaError(rc, "basa_shift_schedule")
+    return [(int(dh[l]), int(dw[l])) for l in range(L)]
 
 
 def version() -> int:

@@ -111,6 +111,29 @@ const char* basa_status_string(int status) {
   }
 }
 
-int basa_version(void) { return (1 << 16) | 0; }
+int basa_version(void) { return (1 << 16) | 1; }
+
+// Interleaved shift schedule, BASA §3.1: per axis the offsets (i * delta) mod w with
+// delta = max(1, floor(w / L)) are taken alternately from their first ceil(L/2) and the
+// remaining entries; the step offset c is added modulo the window side.
+int basa_shift_schedule(int L, int wh, int ww, int ch, int cw, int32_t* dh, int32_t* dw) {
+  if (!dh || !dw) return BASA_ERR_NULL;
+  if (L <= 0 || wh <= 0 || ww <= 0) return BASA_ERR_SHAPE;
+  const int K = (L + 1) / 2;
+  for (int l = 0; l < L; ++l) {
+    // position l of the interleaving holds entry i of the offset sequence
+    const int i = (l % 2 == 0) ? l / 2 : K + l / 2;
+    const int sides[2] = {wh, ww};
+    const int steps[2] = {ch, cw};
+    int32_t* outs[2] = {dh, dw};
+    for (int ax = 0; ax < 2; ++ax) {
+      const int w = sides[ax];
+      const int64_t delta = w / L > 1 ? w / L : 1;
+      const int64_t a = (int64_t(i) * delta) % w;
+      outs[ax][l] = int32_t(reduce_mod(int(a) + reduce_mod(steps[ax], w), w));
+    }
+  }
+  return BASA_OK;
+}
 
 }  // extern "C"
