@@ -1,9 +1,10 @@
 """The five synthetic workloads the path is checked and measured on.
 
 Shapes follow the pages' workloads: FLUX.1-dev latents at 1024^2, 2048^2 and 4096^2
-(16x16 latent patches -> 64x64, 128x128, 256x256 token grids, 24 heads of 128) and a
-Wan2.1-shaped video latent (21 frames of 30x52 tokens, 12 heads of 128), plus a tiny
-fp32 2-D case small enough for exhaustive checks. Each workload lists the shifts of
+(16x16 latent patches -> 64x64, 128x128, 256x256 token grids, 24 heads of 128), a
+Wan2.1-shaped video latent (21 frames of 30x52 tokens, 12 heads of 128), the pages' own
+Wan measurement grid (21 frames of 60x104 tokens), plus a tiny fp32 2-D case small
+enough for exhaustive checks. Each workload lists the shifts of
 its block cycle: the path is called once per shift on the same q, k, v.
 """
 from __future__ import annotations
@@ -66,6 +67,11 @@ WORKLOADS = (
              ((0, 0, 0), (0, 16, 0), (0, 0, 16), (0, 16, 16)), 4),
     Workload("wan-21x30x52-w7x15x26", "bf16", 1, 12, 128, (21, 30, 52), (7, 15, 26),
              ((0, 0, 0), (3, 7, 13)), 5),
+    # The pages' own Wan measurement shape (Table 3): 1664x960 output, 81 frames -> a
+    # 21x60x104 latent grid; windows keep the whole temporal axis (21) with 15x26 spatial
+    # extent, i.e. 16 windows of 8190 tokens.
+    Workload("wan-21x60x104-w21x15x26", "bf16", 1, 12, 128, (21, 60, 104), (21, 15, 26),
+             ((0, 0, 0), (0, 7, 13)), 6),
 )
 
 BY_NAME = {w.name: w for w in WORKLOADS}

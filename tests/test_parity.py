@@ -180,7 +180,7 @@ def test_full_attention_small_every_element():
         assert_parity(got, ref, dtype, f"full {dtype} {shape}")
 
 
-@pytest.mark.parametrize("w", [WORKLOADS[1], WORKLOADS[2], WORKLOADS[4]], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [WORKLOADS[1], WORKLOADS[2], WORKLOADS[4], WORKLOADS[5]], ids=lambda w: w.name)
 def test_full_attention_workload_sampled(w, workload_inputs):
     t, dev = workload_inputs(w)
     log_case(w.name, "basa_full_attn_fwd", w.shape)
