@@ -44,7 +44,7 @@ typedef enum {
   BASA_ERR_NULL = 1,        /* a required pointer is NULL */
   BASA_ERR_SHAPE = 2,       /* non-positive size, or window does not divide the grid */
   BASA_ERR_UNSUPPORTED = 3, /* dtype or head_dim outside the supported set */
-  BASA_ERR_ALIAS = 4,       /* out overlaps q, k or v */
+  BASA_ERR_ALIAS = 4,       /* an output buffer overlaps an input or another output */
   BASA_ERR_OVERFLOW = 5,    /* a size or index does not fit the 32-bit per-head indexing:
                                T*H*W, B*heads and N*head_dim must not exceed 2^31-1, and
                                for bf16 one head must not exceed 0xffffff00 bytes */
@@ -80,6 +80,40 @@ int basa_window_attn_fwd(const void* q, const void* k, const void* v, void* out,
  */
 int basa_full_attn_fwd(const void* q, const void* k, const void* v, void* out,
                        int B, int heads, int N, int head_dim, int dtype, hipStream_t stream);
+
+/*
+ * K/V pooling for the global memory (paper §3.2 "K/V-Pooled Global Memory", first displayed
+ * equation; the count of App. A.1 "Computational complexity"). k, v: [B, heads, T*H*W,
+ * head_dim] as for basa_window_attn_fwd. Every frame t is cut into regions of ph x pw
+ * tokens starting at (h, w) = (0, 0) of the original (unshifted) grid, gh = ceil(H/ph) by
+ * gw = ceil(W/pw) of them; a region cut by the far edge holds only the tokens inside.
+ *   kmem[b, h, (t*gh + i)*gw + j, :] = mean of k over region (i, j) of frame t
+ * (vmem likewise from v), accumulated in fp32 and stored in dtype (bf16: round to nearest
+ * even). kmem, vmem: caller-owned device buffers of B*heads*T*gh*gw*head_dim elements,
+ * 16-byte aligned, not overlapping k, v or each other (BASA_ERR_ALIAS).
+ * Errors as basa_window_attn_fwd; ph, pw must be positive (BASA_ERR_SHAPE).
+ */
+int basa_pool_kv(const void* k, const void* v, void* kmem, void* vmem, int B, int heads, int T, int H, int W,
+                 int ph, int pw, int head_dim, int dtype, hipStream_t stream);
+
+/*
+ * Shifted local-window attention with pooled global memory (paper §3.2, second displayed
+ * equation): the queries of every window attend, in one softmax, to the window's own keys
+ * and values followed by n_mem memory keys and values shared by all windows of a head:
+ *   out[b,h,i,:] = softmax over j in win(i) + memory of (q_i . key_j / sqrt(d)) value_j.
+ * kmem, vmem: [B, heads, n_mem, head_dim] device buffers in dtype (for example from
+ * basa_pool_kv, n_mem = T*gh*gw); n_mem = 0 with NULL kmem/vmem gives
+ * basa_window_attn_fwd's result.
+ * lse: optional (NULL = not written) fp32 device buffer [B, heads, N]: the natural-log
+ * log-sum-exp of each row's scaled logits, so results over disjoint key sets can be
+ * merged as O = (1 - g) O_a + g O_b, g = sigmoid(lse_b - lse_a) (paper App. A.1, last
+ * displayed equation). Grid, window, shift, layout and errors as basa_window_attn_fwd;
+ * additionally out and lse must not overlap any input or each other (BASA_ERR_ALIAS) and
+ * lse must be 4-byte aligned.
+ */
+int basa_window_attn_mem_fwd(const void* q, const void* k, const void* v, const void* kmem, const void* vmem,
+                             int n_mem, void* out, float* lse, int B, int heads, int T, int H, int W, int wt, int wh,
+                             int ww, int st, int sh, int sw, int head_dim, int dtype, hipStream_t stream);
 
 /*
  * Window membership export (paper §3.1): perm[m * Wtok + l] = flat original token of

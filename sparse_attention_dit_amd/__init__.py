@@ -8,9 +8,12 @@ from ._lib import (  # noqa: F401
     BasaError,
     full_attn_fwd,
     load,
+    pool_kv,
+    pooled_count,
     shift_schedule,
     status_string,
     version,
     window_attn_fwd,
+    window_attn_mem_fwd,
     window_perm,
 )

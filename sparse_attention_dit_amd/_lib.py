@@ -17,8 +17,8 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 
 # Exported C symbols, in header order.
-SYMBOLS = ("basa_window_attn_fwd", "basa_full_attn_fwd", "basa_window_perm",
-           "basa_shift_schedule", "basa_status_string", "basa_version")
+SYMBOLS = ("basa_window_attn_fwd", "basa_full_attn_fwd", "basa_pool_kv", "basa_window_attn_mem_fwd",
+           "basa_window_perm", "basa_shift_schedule", "basa_status_string", "basa_version")
 
 
 class BasaError(RuntimeError):
@@ -43,6 +43,10 @@ def load() -> ctypes.CDLL:
     lib.basa_window_attn_fwd.restype = i
     lib.basa_full_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.basa_full_attn_fwd.restype = i
+    lib.basa_pool_kv.argtypes = [vp, vp, vp, vp] + [i] * 9 + [vp]
+    lib.basa_pool_kv.restype = i
+    lib.basa_window_attn_mem_fwd.argtypes = [vp] * 5 + [i, vp, vp] + [i] * 13 + [vp]
+    lib.basa_window_attn_mem_fwd.restype = i
     lib.basa_window_perm.argtypes = [i] * 9 + [vp, vp]
     lib.basa_window_perm.restype = i
     lib.basa_shift_schedule.argtypes = [i] * 5 + [vp, vp]
@@ -112,6 +116,71 @@ def full_attn_fwd(q, k, v, out, stream=None) -> None:
                                    _dtype_code(q), _stream_handle(stream))
     if rc != 0:
         raise BasaError(rc, "basa_full_attn_fwd")
+
+
+def pooled_count(grid, pool) -> int:
+    """Memory tokens per head: T * ceil(H/ph) * ceil(W/pw)."""
+    T, H, W = (int(x) for x in grid)
+    ph, pw = (int(x) for x in pool)
+    return T * (-(-H // ph)) * (-(-W // pw))
+
+
+def pool_kv(k, v, kmem, vmem, grid, pool, stream=None) -> None:
+    """Pooled memory: kmem/vmem [B, heads, T*gh*gw, d] = region means of k/v."""
+    for name, t in (("k", k), ("v", v), ("kmem", kmem), ("vmem", vmem)):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise BasaError(2, f"{name} must be a contiguous 4-D device tensor")
+        if t.dtype != k.dtype:
+            raise BasaError(2, f"{name} dtype {t.dtype} differs from k")
+    if v.shape != k.shape:
+        raise BasaError(2, "k and v shapes differ")
+    B, H_, N, d = k.shape
+    T, H, W = (int(x) for x in grid)
+    if T * H * W != N:
+        raise BasaError(2, f"grid {grid} holds {T * H * W} tokens, tensors hold {N}")
+    G = pooled_count(grid, pool)
+    for name, t in (("kmem", kmem), ("vmem", vmem)):
+        if tuple(t.shape) != (B, H_, G, d):
+            raise BasaError(2, f"{name} must be {(B, H_, G, d)}, got {tuple(t.shape)}")
+    ph, pw = (int(x) for x in pool)
+    rc = load().basa_pool_kv(k.data_ptr(), v.data_ptr(), kmem.data_ptr(), vmem.data_ptr(), B, H_, T, H, W, ph, pw,
+                             d, _dtype_code(k), _stream_handle(stream))
+    if rc != 0:
+        raise BasaError(rc, "basa_pool_kv")
+
+
+def window_attn_mem_fwd(q, k, v, kmem, vmem, out, grid, window, shift, lse=None, stream=None) -> None:
+    """Windowed attention whose keys/values are the window's plus the memory's (kmem,
+    vmem: [B, heads, M, d]; None for no memory); lse: optional fp32 [B, heads, N]."""
+    import torch
+    _check_tensors(q, k, v, out)
+    B, H_, N, d = q.shape
+    n_mem = 0
+    kp = vp_ = 0
+    if kmem is not None or vmem is not None:
+        for name, t in (("kmem", kmem), ("vmem", vmem)):
+            if t is None or not t.is_cuda or not t.is_contiguous() or t.dim() != 4 or t.dtype != q.dtype:
+                raise BasaError(2, f"{name} must be a contiguous 4-D device tensor of q's dtype")
+            if t.shape[0] != B or t.shape[1] != H_ or t.shape[3] != d:
+                raise BasaError(2, f"{name} must be [B, heads, M, d]")
+        if kmem.shape != vmem.shape:
+            raise BasaError(2, "kmem and vmem shapes differ")
+        n_mem, kp, vp_ = int(kmem.shape[2]), kmem.data_ptr(), vmem.data_ptr()
+    lp = 0
+    if lse is not None:
+        if not lse.is_cuda or lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, H_, N):
+            raise BasaError(2, "lse must be a contiguous float32 device tensor [B, heads, N]")
+        lp = lse.data_ptr()
+    T, H, W = (int(x) for x in grid)
+    if T * H * W != N:
+        raise BasaError(2, f"grid {grid} holds {T * H * W} tokens, tensors hold {N}")
+    wt, wh, ww = (int(x) for x in window)
+    st, sh, sw = (int(x) for x in shift)
+    rc = load().basa_window_attn_mem_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), kp or None, vp_ or None, n_mem,
+                                         out.data_ptr(), lp or None, B, H_, T, H, W, wt, wh, ww, st, sh, sw, d,
+                                         _dtype_code(q), _stream_handle(stream))
+    if rc != 0:
+        raise BasaError(rc, "basa_window_attn_mem_fwd")
 
 
 def window_perm(grid, window, shift, perm, stream=None) -> None:

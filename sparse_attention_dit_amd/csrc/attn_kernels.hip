@@ -6,7 +6,9 @@
 // App. A.1 runs this as roll + reshape/permute copies + batched SDPA; here the roll, the
 // partition and the inverse roll are folded into the kernel's row addressing: each
 // workgroup reads its window's rows straight from their original positions and writes
-// the outputs straight back to them, so there is no copy pass.
+// the outputs straight back to them, so there is no copy pass. Optionally (§3.2) every
+// window's keys and values are followed by a shared set of pooled memory tokens, and the
+// per-row log-sum-exp is written for merging with other attention results (App. A.1).
 //
 // bf16 kernel layout (one workgroup = one (batch*head, window, query tile)):
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q rows kept
@@ -17,9 +19,9 @@
 //     row swapped) so that the accumulator registers 8c..8c+7 of lane half h hold the
 //     probabilities of 8 consecutive keys 16c + 8h .. 16c + 8h + 7. Packed to bf16 they
 //     are, unchanged, the B operand of O^T = V^T P^T.
-//   * V is transposed into LDS (Vt[d][key]) so the A operand of O^T = V^T P^T is one
-//     16-byte LDS read. The d rows of Vt are assigned so each lane's O^T registers are
-//     head_dim/2 consecutive output elements of its query row.
+//   * V stays row-major in LDS; gfx950's transposing LDS read (ds_read_b64_tr_b16)
+//     delivers the A operand of O^T = V^T P^T. The d rows are assigned so each lane's
+//     O^T registers are head_dim/2 consecutive output elements of its query row.
 //   * Online softmax in fp32 with exp2 and the 1/sqrt(d)*log2(e) scale folded into one
 //     FMA; the running max is only raised (and O rescaled) when a row's max grows by
 //     more than 2^8, which keeps the final O/l exact while skipping most rescales.
@@ -168,6 +170,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const uint32_t head_bytes = uint32_t(p.head_stride) * 2u;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + base, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + base, head_bytes);
+  // The key/value stream is the window's Tw tiles, then (§3.2) mem_tiles tiles of the
+  // pooled memory, a plain [n_mem, D] block per head.
+  const int Tw = p.kv_tiles;
+  const int Tn = Tw + p.mem_tiles;
+  const int64_t mem_base = int64_t(tile.bh) * int64_t(p.n_mem) * D;
+  const uint32_t mem_bytes = uint32_t(p.n_mem) * uint32_t(L::ROW_BYTES);
+  const __amdgpu_buffer_rsrc_t kmrs = make_rsrc(static_cast<const uint16_t*>(p.kmem) + mem_base, mem_bytes);
+  const __amdgpu_buffer_rsrc_t vmrs = make_rsrc(static_cast<const uint16_t*>(p.vmem) + mem_base, mem_bytes);
 
   // ---- K/V tile loads: wave `wave` fills row groups wave*LOADS .. +LOADS-1 of both tiles.
   // Lane j moves 16 bytes: chunk slot j / RPG of row (group*RPG + j % RPG).
@@ -180,12 +190,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   auto row_offset = [&](int local) __attribute__((always_inline)) -> uint32_t {
     return local < p.wtok ? uint32_t(token_of(p.map, org, uint32_t(local))) * uint32_t(L::ROW_BYTES) : 0xffffff00u;
   };
-  auto dma_tile = [&](const uint32_t* row_off, char* st) __attribute__((always_inline)) {
+  // Byte offset of row r of key/value tile t (window tile, or memory tile past Tw).
+  auto tile_row_offset = [&](int t, int r) __attribute__((always_inline)) -> uint32_t {
+    if (t < Tw) return row_offset(t * BN + r);
+    const int j = (t - Tw) * BN + r;
+    return j < p.n_mem ? uint32_t(j) * uint32_t(L::ROW_BYTES) : 0xffffff00u;
+  };
+  auto dma_tile = [&](const uint32_t* row_off, char* st, int t) __attribute__((always_inline)) {
+    const bool mem = t >= Tw;
+    const __amdgpu_buffer_rsrc_t ks = mem ? kmrs : krs;
+    const __amdgpu_buffer_rsrc_t vs = mem ? vmrs : vrs;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int g = wave * C::LOADS + i;
-      dma16_to_lds(krs, st + g * RG, row_off[i] + k_chunk_off);
-      dma16_to_lds(vrs, st + C::TILE_BYTES + g * RG, row_off[i] + v_chunk_off);
+      dma16_to_lds(ks, st + g * RG, row_off[i] + k_chunk_off);
+      dma16_to_lds(vs, st + C::TILE_BYTES + g * RG, row_off[i] + v_chunk_off);
     }
   };
   // The row offsets of the K/V tiles are computed cooperatively a few tiles ahead into a
@@ -198,7 +217,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   auto fill_tab = [&](int first, int ntiles) __attribute__((always_inline)) {
     for (int e = tid; e < ntiles * BN; e += C::NT) {
       const int t = first + e / BN;
-      rowtab[(t % TAB_TILES) * BN + e % BN] = row_offset(t * BN + e % BN);
+      rowtab[(t % TAB_TILES) * BN + e % BN] = tile_row_offset(t, e % BN);
     }
   };
   auto read_offs = [&](int t, uint32_t* row_off) __attribute__((always_inline)) {
@@ -211,9 +230,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     uint32_t off0[C::LOADS];
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) off0[i] = row_offset((wave * C::LOADS + i) * RPG + ld_row);
-    dma_tile(off0, stage0);
+    dma_tile(off0, stage0, 0);
   }
-  fill_tab(0, min(TAB_TILES, p.kv_tiles));
+  fill_tab(0, min(TAB_TILES, Tn));
 
   // ---- Q: each wave DMAs its own 32 rows into the Q buffer (laid out like a K tile, 4 whole
   // rows per wave-wide load), and after the prologue barrier reads its fragments from there.
@@ -263,12 +282,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // holds the row offsets of tile t+1 (read from the table during the previous step).
   uint32_t next_off[C::LOADS];
   auto tile_step = [&](int t, const char* cur, char* nxt) {
-    if (t + 1 < p.kv_tiles) dma_tile(next_off, nxt);
-    if (t + 2 < p.kv_tiles) read_offs(t + 2, next_off);
+    if (t + 1 < Tn) dma_tile(next_off, nxt, t + 1);
+    if (t + 2 < Tn) read_offs(t + 2, next_off);
     // refill the ring slots of tiles t-8 .. t-1 (all issued) with tiles t+8 .. t+15, first
     // needed by the DMA of step t+7; the barrier ending this step publishes them
-    if (t % REFILL == 0 && t >= REFILL && t + REFILL < p.kv_tiles)
-      fill_tab(t + REFILL, min(REFILL, p.kv_tiles - t - REFILL));
+    if (t % REFILL == 0 && t >= REFILL && t + REFILL < Tn) fill_tab(t + REFILL, min(REFILL, Tn - t - REFILL));
     const char* ks = cur;
     const char* vs = cur + C::TILE_BYTES;
 
@@ -291,9 +309,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       for (int kb = 0; kb < 2; ++kb)
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk][kb], qf[kk], sacc[kb], 0, 0, 0);
 
-    // ragged last tile: keys past the window get -inf
-    if ((t + 1) * BN > p.wtok) {
-      const int lim = p.wtok - t * BN;
+    // ragged last tile of the window or of the memory: keys past the end get -inf
+    const int lim = t < Tw ? p.wtok - t * BN : p.n_mem - (t - Tw) * BN;
+    if (lim < BN) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -369,10 +387,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   __syncthreads();  // tile 0 and Q resident, row tables written
 #pragma unroll
   for (int kk = 0; kk < DK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qbuf + q_rd + kk * CS);
-  if (1 < p.kv_tiles) read_offs(1, next_off);
-  for (int t = 0; t < p.kv_tiles; t += 2) {
+  if (1 < Tn) read_offs(1, next_off);
+  for (int t = 0; t < Tn; t += 2) {
     tile_step(t, stage0, stage1);
-    if (t + 1 < p.kv_tiles) tile_step(t + 1, stage1, stage0);
+    if (t + 1 < Tn) tile_step(t + 1, stage1, stage0);
   }
 
   // ---- normalise and store each row at its original (un-shifted) position. The packed rows
@@ -400,6 +418,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int i = 0; i < QG; ++i)
       buffer_store16(ors, qrowtab[(wave * QG + i) * RPG + ld_row] + k_chunk_off, w[i]);
+    // log-sum-exp of the row's scaled logits, natural log: (m + log2 l) * ln 2
+    if (p.lse != nullptr && hh == 0 && tile.qtile * BM + qrow < p.wtok) {
+      const uint32_t tok = qrowtab[qrow] / uint32_t(L::ROW_BYTES);
+      p.lse[int64_t(tile.bh) * p.n_tokens + tok] = (m_run + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
+    }
   }
 }
 
@@ -436,19 +459,33 @@ __global__ __launch_bounds__(64) void win_attn_f32_kernel(const float* __restric
   float m = -__builtin_inff(), l = 0.0f;
   const float c = p.scale_log2;
 
-  for (int t = 0; t * BN < p.wtok; ++t) {
+  // key/value tiles: the window's, then (§3.2) those of the pooled memory
+  const int Tw = (p.wtok + BN - 1) / BN;
+  const int Tn = Tw + (p.n_mem + BN - 1) / BN;
+  const float* kmem = static_cast<const float*>(p.kmem) + int64_t(tile.bh) * int64_t(p.n_mem) * D;
+  const float* vmem = static_cast<const float*>(p.vmem) + int64_t(tile.bh) * int64_t(p.n_mem) * D;
+  for (int t = 0; t < Tn; ++t) {
+    const bool mem = t >= Tw;
+    const int nrows = mem ? p.n_mem - (t - Tw) * BN : p.wtok - t * BN;
     __syncthreads();
     // 64 lanes load 32 rows: two lanes per row, each half of the row
     {
       const int r = lane >> 1;
       const int half = lane & 1;
-      const int local = t * BN + r;
       float* kd = &Ks[r * D + half * (D / 2)];
       float* vd = &Vs[r * D + half * (D / 2)];
-      if (local < p.wtok) {
-        const int tok = token_of(p.map, org, uint32_t(local));
-        const float* ks = k + base + int64_t(tok) * D + half * (D / 2);
-        const float* vs = v + base + int64_t(tok) * D + half * (D / 2);
+      if (r < nrows) {
+        const float* ks;
+        const float* vs;
+        if (mem) {
+          const int64_t j = int64_t((t - Tw) * BN + r) * D + half * (D / 2);
+          ks = kmem + j;
+          vs = vmem + j;
+        } else {
+          const int tok = token_of(p.map, org, uint32_t(t * BN + r));
+          ks = k + base + int64_t(tok) * D + half * (D / 2);
+          vs = v + base + int64_t(tok) * D + half * (D / 2);
+        }
 #pragma unroll
         for (int d = 0; d < D / 2; ++d) {
           kd[d] = ks[d];
@@ -463,7 +500,7 @@ __global__ __launch_bounds__(64) void win_attn_f32_kernel(const float* __restric
       }
     }
     __syncthreads();
-    const int nk = min(BN, p.wtok - t * BN);
+    const int nk = min(BN, nrows);
     for (int j0 = 0; j0 < nk; j0 += CH) {
       float s[CH];
       float mx = -__builtin_inff();
@@ -494,6 +531,8 @@ __global__ __launch_bounds__(64) void win_attn_f32_kernel(const float* __restric
     const float inv = 1.0f / l;
 #pragma unroll
     for (int d = 0; d < D; ++d) out[base + int64_t(my_tok) * D + d] = o[d] * inv;
+    if (p.lse != nullptr)
+      p.lse[int64_t(tile.bh) * p.n_tokens + my_tok] = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
   }
 }
 
@@ -507,12 +546,93 @@ __global__ void win_perm_kernel(WinMap map, int32_t wtok, int32_t total, int32_t
 }
 
 // ---------------------------------------------------------------------------------
+// K/V pooling (BASA §3.2): one thread per (bh, frame, region, 16-byte chunk of the row).
+// Consecutive threads take consecutive chunks of one region, so each token row of the
+// region is read as whole coalesced rows; the mean is accumulated in fp32 and stored in
+// the tensor's type (bf16: round to nearest even). blockIdx.y selects k (0) or v (1).
+template <int D, typename T>
+__global__ __launch_bounds__(256) void pool_kv_kernel(const T* __restrict__ k, const T* __restrict__ v,
+                                                      T* __restrict__ kmem, T* __restrict__ vmem, int32_t bh_total,
+                                                      int32_t nT, int32_t H, int32_t W, int32_t ph, int32_t pw,
+                                                      int32_t gh, int32_t gw) {
+  constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
+  constexpr int CPR = D / EPC;         // chunks per row
+  const T* src = blockIdx.y == 0 ? k : v;
+  T* dst = blockIdx.y == 0 ? kmem : vmem;
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t G = int64_t(gh) * gw;
+  const int64_t total = int64_t(bh_total) * nT * G * CPR;
+  if (idx >= total) return;
+  const int chunk = int(idx % CPR);
+  const int64_t region = idx / CPR;  // (bh, t, i, j) row-major
+  const int j = int(region % gw);
+  const int i = int((region / gw) % gh);
+  const int64_t frame = region / G;  // bh * nT + t
+  const int h0 = i * ph, w0 = j * pw;
+  const int h1 = min(h0 + ph, H), w1 = min(w0 + pw, W);
+  float acc[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.0f;
+  for (int h = h0; h < h1; ++h) {
+    const T* row = src + ((frame * H + h) * W + w0) * D + chunk * EPC;
+    for (int w = w0; w < w1; ++w, row += D) {
+      if constexpr (sizeof(T) == 2) {
+        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(row);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += __uint_as_float(x[e] << 16);
+          acc[2 * e + 1] += __uint_as_float(x[e] & 0xffff0000u);
+        }
+      } else {
+        const float4 x = *reinterpret_cast<const float4*>(row);
+        acc[0] += x.x;
+        acc[1] += x.y;
+        acc[2] += x.z;
+        acc[3] += x.w;
+      }
+    }
+  }
+  const float inv = 1.0f / float((h1 - h0) * (w1 - w0));
+  T* o = dst + region * D + chunk * EPC;
+  if constexpr (sizeof(T) == 2) {
+    u32x4_t y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+    *reinterpret_cast<u32x4_t*>(o) = y;
+  } else {
+    *reinterpret_cast<float4*>(o) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  }
+}
+
+hipError_t launch_pool_kv(const void* k, const void* v, void* kmem, void* vmem, int32_t bh, int32_t T, int32_t H,
+                          int32_t W, int32_t ph, int32_t pw, int head_dim, bool bf16, hipStream_t stream) {
+  const int32_t gh = (H + ph - 1) / ph, gw = (W + pw - 1) / pw;
+  const int epc = bf16 ? 8 : 4;
+  const uint64_t threads = uint64_t(bh) * uint64_t(T) * uint64_t(gh) * uint64_t(gw) * uint64_t(head_dim / epc);
+  const uint64_t blocks = (threads + 255) / 256;
+  if (blocks == 0 || blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
+  const dim3 grid(uint32_t(blocks), 2);
+#define BASA_POOL(DD, TT)                                                                                      \
+  hipLaunchKernelGGL((pool_kv_kernel<DD, TT>), grid, dim3(256), 0, stream, static_cast<const TT*>(k),        \
+                     static_cast<const TT*>(v), static_cast<TT*>(kmem), static_cast<TT*>(vmem), bh, T, H, W, ph, \
+                     pw, gh, gw)
+  if (bf16 && head_dim == 128) BASA_POOL(128, uint16_t);
+  else if (bf16 && head_dim == 64) BASA_POOL(64, uint16_t);
+  else if (!bf16 && head_dim == 128) BASA_POOL(128, float);
+  else if (!bf16 && head_dim == 64) BASA_POOL(64, float);
+  else return hipErrorInvalidValue;
+#undef BASA_POOL
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------
 template <int D, int NW>
 static hipError_t launch_bf16(const void* q, const void* k, const void* v, void* out, AttnParams p,
                               hipStream_t stream) {
   using C = Bf16Cfg<D, NW>;
   p.q_tiles = (p.wtok + C::BM - 1) / C::BM;
   p.kv_tiles = (p.wtok + C::BN - 1) / C::BN;
+  p.mem_tiles = (p.n_mem + C::BN - 1) / C::BN;
   const uint64_t blocks = uint64_t(p.q_tiles) * uint64_t(p.n_win) * uint64_t(p.heads_total);
   if (blocks == 0 || blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((win_attn_bf16_kernel<D, NW>), dim3(uint32_t(blocks)), dim3(C::NT), 0, stream,
@@ -526,6 +646,7 @@ static hipError_t launch_f32(const void* q, const void* k, const void* v, void* 
                              hipStream_t stream) {
   p.q_tiles = (p.wtok + 63) / 64;
   p.kv_tiles = (p.wtok + 31) / 32;
+  p.mem_tiles = (p.n_mem + 31) / 32;
   const uint64_t blocks = uint64_t(p.q_tiles) * uint64_t(p.n_win) * uint64_t(p.heads_total);
   if (blocks == 0 || blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((win_attn_f32_kernel<D>), dim3(uint32_t(blocks)), dim3(64), 0, stream,

@@ -19,11 +19,23 @@ struct AttnParams {
   int32_t heads_total;  // B * heads
   int64_t head_stride;  // N * head_dim elements
   float scale_log2;     // log2(e) / sqrt(head_dim)
+  // K/V-pooled global memory appended to every window's keys (n_mem = 0: none), laid out
+  // [B*heads, n_mem, head_dim] like k and v; mem_tiles is filled by the launcher
+  const void* kmem;
+  const void* vmem;
+  int32_t n_mem;
+  int32_t mem_tiles;
+  float* lse;           // optional [B*heads, N] natural-log log-sum-exp of each row's logits
+  int32_t n_tokens;     // N
 };
 
 hipError_t launch_window_attention(const void* q, const void* k, const void* v, void* out, const AttnParams& p,
                                    int head_dim, bool bf16, hipStream_t stream);
 
 hipError_t launch_window_perm(const WinMap& map, int32_t wtok, int32_t total, int32_t* perm, hipStream_t stream);
+
+// Pooled memory: kmem/vmem [BH, T*gh*gw, D] = means of k/v over ph x pw regions per frame.
+hipError_t launch_pool_kv(const void* k, const void* v, void* kmem, void* vmem, int32_t bh, int32_t T, int32_t H,
+                          int32_t W, int32_t ph, int32_t pw, int head_dim, bool bf16, hipStream_t stream);
 
 }  // namespace basa

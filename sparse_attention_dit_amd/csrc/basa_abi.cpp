@@ -27,6 +27,11 @@ bool overlaps(const void* a, const void* b, int64_t bytes) {
   return x < y + uint64_t(bytes) && y < x + uint64_t(bytes);
 }
 
+bool overlaps2(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + uint64_t(bbytes) && y < x + uint64_t(abytes);
+}
+
 int check_grid(int T, int H, int W, int wt, int wh, int ww) {
   if (T <= 0 || H <= 0 || W <= 0 || wt <= 0 || wh <= 0 || ww <= 0) return BASA_ERR_SHAPE;
   if (T % wt || H % wh || W % ww) return BASA_ERR_SHAPE;
@@ -34,9 +39,13 @@ int check_grid(int T, int H, int W, int wt, int wh, int ww) {
   return BASA_OK;
 }
 
-int run_attention(const void* q, const void* k, const void* v, void* out, int B, int heads, int T, int H, int W,
-                  int wt, int wh, int ww, int st, int sh, int sw, int head_dim, int dtype, hipStream_t stream) {
+// Memory (kmem, vmem, n_mem) and lse are optional: n_mem = 0 with null kmem/vmem, lse null.
+int run_attention(const void* q, const void* k, const void* v, const void* kmem, const void* vmem, int n_mem,
+                  void* out, float* lse, int B, int heads, int T, int H, int W, int wt, int wh, int ww, int st,
+                  int sh, int sw, int head_dim, int dtype, hipStream_t stream) {
   if (!q || !k || !v || !out) return BASA_ERR_NULL;
+  if (n_mem < 0) return BASA_ERR_SHAPE;
+  if (n_mem > 0 && (!kmem || !vmem)) return BASA_ERR_NULL;
   if (dtype != BASA_DTYPE_F32 && dtype != BASA_DTYPE_BF16) return BASA_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return BASA_ERR_UNSUPPORTED;
   if (B <= 0 || heads <= 0) return BASA_ERR_SHAPE;
@@ -49,10 +58,25 @@ int run_attention(const void* q, const void* k, const void* v, void* out, int B,
   // reads rows past a window at byte offsets from 0xffffff00 up, which must lie outside the
   // head's range to read as zeros.
   if (dtype == BASA_DTYPE_BF16 && N * head_dim * 2 > int64_t(kBf16HeadBytesMax)) return BASA_ERR_OVERFLOW;
+  if (int64_t(n_mem) * head_dim > kInt32Max) return BASA_ERR_OVERFLOW;
+  if (dtype == BASA_DTYPE_BF16 && int64_t(n_mem) * head_dim * 2 > int64_t(kBf16HeadBytesMax)) return BASA_ERR_OVERFLOW;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return BASA_ERR_ALIGN;
+  if (n_mem > 0 && (!aligned(kmem, 16) || !aligned(vmem, 16))) return BASA_ERR_ALIGN;
+  if (lse && !aligned(lse, 4)) return BASA_ERR_ALIGN;
   const int64_t elem = dtype == BASA_DTYPE_BF16 ? 2 : 4;
   const int64_t bytes = bh * N * head_dim * elem;
+  const int64_t mem_bytes = bh * int64_t(n_mem) * head_dim * elem;
   if (overlaps(out, q, bytes) || overlaps(out, k, bytes) || overlaps(out, v, bytes)) return BASA_ERR_ALIAS;
+  if (n_mem > 0 && (overlaps2(out, bytes, kmem, mem_bytes) || overlaps2(out, bytes, vmem, mem_bytes)))
+    return BASA_ERR_ALIAS;
+  if (lse) {
+    const int64_t lse_bytes = bh * N * 4;
+    if (overlaps2(lse, lse_bytes, q, bytes) || overlaps2(lse, lse_bytes, k, bytes) ||
+        overlaps2(lse, lse_bytes, v, bytes) || overlaps2(lse, lse_bytes, out, bytes))
+      return BASA_ERR_ALIAS;
+    if (n_mem > 0 && (overlaps2(lse, lse_bytes, kmem, mem_bytes) || overlaps2(lse, lse_bytes, vmem, mem_bytes)))
+      return BASA_ERR_ALIAS;
+  }
 
   basa::AttnParams p;
   p.map = basa::make_winmap(T, H, W, wt, wh, ww, reduce_mod(st, T), reduce_mod(sh, H), reduce_mod(sw, W));
@@ -63,6 +87,12 @@ int run_attention(const void* q, const void* k, const void* v, void* out, int B,
   p.heads_total = int32_t(bh);
   p.head_stride = N * head_dim;
   p.scale_log2 = float(1.4426950408889634 / sqrt(double(head_dim)));
+  p.kmem = n_mem > 0 ? kmem : nullptr;
+  p.vmem = n_mem > 0 ? vmem : nullptr;
+  p.n_mem = n_mem;
+  p.mem_tiles = 0;
+  p.lse = lse;
+  p.n_tokens = int32_t(N);
   const hipError_t e =
       basa::launch_window_attention(q, k, v, out, p, head_dim, dtype == BASA_DTYPE_BF16, stream);
   if (e == hipErrorInvalidConfiguration) return BASA_ERR_OVERFLOW;
@@ -76,12 +106,44 @@ extern "C" {
 int basa_window_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int heads, int T, int H,
                          int W, int wt, int wh, int ww, int st, int sh, int sw, int head_dim, int dtype,
                          hipStream_t stream) {
-  return run_attention(q, k, v, out, B, heads, T, H, W, wt, wh, ww, st, sh, sw, head_dim, dtype, stream);
+  return run_attention(q, k, v, nullptr, nullptr, 0, out, nullptr, B, heads, T, H, W, wt, wh, ww, st, sh, sw,
+                       head_dim, dtype, stream);
 }
 
 int basa_full_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int heads, int N,
                        int head_dim, int dtype, hipStream_t stream) {
-  return run_attention(q, k, v, out, B, heads, 1, 1, N, 1, 1, N, 0, 0, 0, head_dim, dtype, stream);
+  return run_attention(q, k, v, nullptr, nullptr, 0, out, nullptr, B, heads, 1, 1, N, 1, 1, N, 0, 0, 0, head_dim,
+                       dtype, stream);
+}
+
+int basa_window_attn_mem_fwd(const void* q, const void* k, const void* v, const void* kmem, const void* vmem,
+                             int n_mem, void* out, float* lse, int B, int heads, int T, int H, int W, int wt, int wh,
+                             int ww, int st, int sh, int sw, int head_dim, int dtype, hipStream_t stream) {
+  return run_attention(q, k, v, kmem, vmem, n_mem, out, lse, B, heads, T, H, W, wt, wh, ww, st, sh, sw, head_dim,
+                       dtype, stream);
+}
+
+int basa_pool_kv(const void* k, const void* v, void* kmem, void* vmem, int B, int heads, int T, int H, int W,
+                 int ph, int pw, int head_dim, int dtype, hipStream_t stream) {
+  if (!k || !v || !kmem || !vmem) return BASA_ERR_NULL;
+  if (dtype != BASA_DTYPE_F32 && dtype != BASA_DTYPE_BF16) return BASA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return BASA_ERR_UNSUPPORTED;
+  if (B <= 0 || heads <= 0 || T <= 0 || H <= 0 || W <= 0 || ph <= 0 || pw <= 0) return BASA_ERR_SHAPE;
+  const int64_t bh = int64_t(B) * heads;
+  const int64_t N = int64_t(T) * H * W;
+  if (bh > kInt32Max || N * head_dim > kInt32Max) return BASA_ERR_OVERFLOW;
+  const int64_t G = int64_t(T) * ((H + ph - 1) / ph) * ((W + pw - 1) / pw);
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(kmem, 16) || !aligned(vmem, 16)) return BASA_ERR_ALIGN;
+  const int64_t elem = dtype == BASA_DTYPE_BF16 ? 2 : 4;
+  const int64_t in_bytes = bh * N * head_dim * elem, out_bytes = bh * G * head_dim * elem;
+  if (overlaps2(kmem, out_bytes, k, in_bytes) || overlaps2(kmem, out_bytes, v, in_bytes) ||
+      overlaps2(vmem, out_bytes, k, in_bytes) || overlaps2(vmem, out_bytes, v, in_bytes) ||
+      overlaps2(kmem, out_bytes, vmem, out_bytes))
+    return BASA_ERR_ALIAS;
+  const hipError_t e = basa::launch_pool_kv(k, v, kmem, vmem, int32_t(bh), T, H, W, ph, pw, head_dim,
+                                            dtype == BASA_DTYPE_BF16, stream);
+  if (e == hipErrorInvalidConfiguration) return BASA_ERR_OVERFLOW;
+  return e == hipSuccess ? BASA_OK : BASA_ERR_HIP;
 }
 
 int basa_window_perm(int T, int H, int W, int wt, int wh, int ww, int st, int sh, int sw, int32_t* perm,
@@ -103,7 +165,7 @@ const char* basa_status_string(int status) {
     case BASA_ERR_NULL: return "a required pointer is NULL";
     case BASA_ERR_SHAPE: return "non-positive size, or the window does not divide the grid";
     case BASA_ERR_UNSUPPORTED: return "unsupported dtype or head_dim (supported: f32/bf16 x 64/128)";
-    case BASA_ERR_ALIAS: return "out overlaps q, k or v";
+    case BASA_ERR_ALIAS: return "an output buffer overlaps an input or another output";
     case BASA_ERR_OVERFLOW: return "size exceeds the 32-bit per-head indexing";
     case BASA_ERR_HIP: return "HIP launch error";
     case BASA_ERR_ALIGN: return "tensor pointer is not 16-byte aligned (perm: 4-byte)";
@@ -111,7 +173,7 @@ const char* basa_status_string(int status) {
   }
 }
 
-int basa_version(void) { return (1 << 16) | 1; }
+int basa_version(void) { return (1 << 16) | 2; }
 
 // Interleaved shift schedule, BASA §3.1: per axis the offsets (i * delta) mod w with
 // delta = max(1, floor(w / L)) are taken alternately from their first ceil(L/2) and the

@@ -89,6 +89,31 @@ def test_full_and_perm_argument_errors():
     assert lib.basa_window_perm(1, 16, 16, 1, 8, 8, 0, 0, 0, A + 2, None) == 7
 
 
+def test_memory_and_pool_argument_errors():
+    lib = _lib.load()
+    E, F = 0x50000000, 0x60000000  # fake memory buffers, far from A..D
+
+    def mem(q=A, k=Bp, v=Cp, km=E, vm=F, n_mem=16, out=D, lse=None, dtype=1, d=128):
+        return lib.basa_window_attn_mem_fwd(q, k, v, km, vm, n_mem, out, lse, 1, 2, 1, 16, 16, 1, 8, 8, 0, 4, 4, d,
+                                            dtype, None)
+    assert mem(n_mem=-1) == 2
+    assert mem(km=None) == 1 and mem(vm=None) == 1
+    assert mem(km=E + 8) == 7
+    assert mem(lse=D + 2) == 7
+    assert mem(lse=A) == 4            # lse over q
+    assert mem(out=E) == 4            # out over the memory
+    assert mem(d=96) == 3
+    assert mem(n_mem=(0xffffff00 // 256) + 1) == 5   # bf16 memory beyond the 32-bit byte range
+
+    def pool(k=A, v=Bp, km=E, vm=F, ph=4, pw=4, dtype=1, d=128):
+        return lib.basa_pool_kv(k, v, km, vm, 1, 2, 1, 16, 16, ph, pw, d, dtype, None)
+    assert pool(k=None) == 1 and pool(vm=None) == 1
+    assert pool(ph=0) == 2 and pool(pw=-1) == 2
+    assert pool(dtype=5) == 3 and pool(d=32) == 3
+    assert pool(km=E + 4) == 7
+    assert pool(km=A) == 4 and pool(vm=E) == 4
+
+
 @pytest.fixture(scope="module")
 def index_tool(tmp_path_factory):
     exe = str(tmp_path_factory.mktemp("idx") / "index_map_check")
