@@ -8,7 +8,7 @@ protocol (§4 / App. A.2 "Implementation and latency measurement"): warm-up firs
 events around the timed region, synchronisation before reading them.
 
 Prints ONE JSON line (rank 0). Usage:
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--cold]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--cold] [--pool P]
 """
 from __future__ import annotations
 
@@ -47,11 +47,13 @@ def measured_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, min_s: float):
+def cpu_baseline(w, min_s: float, pool: int = 0):
     """Time the fp64 oracle (as it stands) on a bounded sample of the workload: whole
-    (shift, head) slices of the windowed attention, in step order and cycling, until at
-    least min_s of CPU work."""
+    (shift, head) slices of the windowed attention (with pooled memory when pool > 0; the
+    pooling itself is done once, untimed), in step order and cycling, until at least min_s
+    of CPU work."""
     from oracle import basa_oracle as O
+    from oracle import memory_oracle as MO
     from sparse_attention_dit_amd import inputs
     try:
         from threadpoolctl import threadpool_info
@@ -60,13 +62,21 @@ def cpu_baseline(w, min_s: float):
         threads = None
     t = inputs.draw_qkv((w.batch, 1, w.tokens, w.head_dim), w.dtype, seed=w.seed)
     q, k, v = (t.exact[n] for n in "qkv")
+    n_mem = 0
+    if pool:
+        km, vm = MO.pool_kv(k, w.grid, (pool, pool)), MO.pool_kv(v, w.grid, (pool, pool))
+        n_mem = km.shape[2]
     slices, elapsed = 0, 0.0
     while elapsed < min_s:
+        shift = w.shifts[(slices // w.heads) % len(w.shifts)]
         t0 = time.perf_counter()
-        O.window_attention(q, k, v, w.grid, w.window, w.shifts[(slices // w.heads) % len(w.shifts)])
+        if pool:
+            MO.window_attention_memory(q, k, v, km, vm, w.grid, w.window, shift)
+        else:
+            O.window_attention(q, k, v, w.grid, w.window, shift)
         elapsed += time.perf_counter() - t0
         slices += 1
-    flops = 4 * w.batch * slices * w.tokens * w.window_tokens * w.head_dim
+    flops = 4 * w.batch * slices * w.tokens * (w.window_tokens + n_mem) * w.head_dim
     return {
         "value": flops / elapsed / 1e12,
         "unit": "TFLOP/s",
@@ -88,6 +98,8 @@ def main():
     ap.add_argument("--full-iters", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline leg")
     ap.add_argument("--cold", action="store_true", help="also time HBM-cold launches (L2/MALL flushed between)")
+    ap.add_argument("--pool", type=int, default=0,
+                    help="with pooled global memory of p x p regions (0: plain windowed attention)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU work timed for cpu_baseline")
     args = ap.parse_args()
 
@@ -112,10 +124,24 @@ def main():
     del t
     out = torch.empty_like(dev["q"])
     stream = torch.cuda.current_stream()
+    n_mem = 0
+    if args.pool:
+        # K/V-pooled global memory (§3.2): pooled once per step (it does not depend on the
+        # shift), then every shift's windows attend to window + memory keys
+        pool = (args.pool, args.pool)
+        n_mem = _lib.pooled_count(w.grid, pool)
+        kmem = torch.empty((w.batch, w.heads, n_mem, w.head_dim), dtype=dev["k"].dtype, device="cuda")
+        vmem = torch.empty_like(kmem)
 
-    def step():
-        for s in w.shifts:
-            _lib.window_attn_fwd(dev["q"], dev["k"], dev["v"], out, w.grid, w.window, s, stream)
+        def step():
+            _lib.pool_kv(dev["k"], dev["v"], kmem, vmem, w.grid, pool, stream)
+            for s in w.shifts:
+                _lib.window_attn_mem_fwd(dev["q"], dev["k"], dev["v"], kmem, vmem, out, w.grid, w.window, s,
+                                         stream=stream)
+    else:
+        def step():
+            for s in w.shifts:
+                _lib.window_attn_fwd(dev["q"], dev["k"], dev["v"], out, w.grid, w.window, s, stream)
 
     # The GPU's clocks need tens of milliseconds of sustained work to ramp up: before the W
     # warm-up steps, run untimed steps for ~0.5 s (sized from one step), reported as
@@ -150,10 +176,23 @@ def main():
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(args.steps):
-            _lib.window_attn_fwd(dev["q"], dev["k"], dev["v"], out, w.grid, w.window, s, stream)
+            if args.pool:
+                _lib.window_attn_mem_fwd(dev["q"], dev["k"], dev["v"], kmem, vmem, out, w.grid, w.window, s,
+                                         stream=stream)
+            else:
+                _lib.window_attn_fwd(dev["q"], dev["k"], dev["v"], out, w.grid, w.window, s, stream)
         e1.record(stream)
         torch.cuda.synchronize()
         per_shift_ms.append(round(e0.elapsed_time(e1) / args.steps, 4))
+    pool_ms = None
+    if args.pool:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            _lib.pool_kv(dev["k"], dev["v"], kmem, vmem, w.grid, pool, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pool_ms = e0.elapsed_time(e1) / args.steps
 
     cold = None
     if args.cold:
@@ -189,10 +228,12 @@ def main():
     torch.cuda.synchronize()
     ms_full = fs.elapsed_time(fe) / args.full_iters
 
-    flops_launch = w.window_flops()
+    # attention FLOPs per launch: 4*B*h*N*(W + M)*d, M = memory tokens (0 without --pool);
+    # with --pool a "launch" is one shift's attention plus its share of the pooling
+    flops_launch = 4 * w.batch * w.heads * w.tokens * (w.window_tokens + n_mem) * w.head_dim
     tflops = flops_launch / (ms_per_launch * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
-    theoretical = w.tokens / w.window_tokens
+    theoretical = w.tokens / (w.window_tokens + n_mem)
     measured = ms_full / ms_per_launch
     io_gbs = w.io_bytes() / (ms_per_launch * 1e-3) / 1e9
 
@@ -224,10 +265,17 @@ def main():
         "io_gbs": round(io_gbs, 1),
         "kernel_hash": kernel_hash(),
     }
+    if args.pool:
+        G_bytes = 2 * w.batch * w.heads * n_mem * w.head_dim * (2 if w.dtype == "bf16" else 4)
+        rec["config"]["pool"] = [args.pool, args.pool]
+        rec["config"]["memory_tokens"] = n_mem
+        rec["pool"] = {"pool_ms": round(pool_ms, 4),
+                       "pool_gbs": round((w.io_bytes() // 2 + G_bytes) / (pool_ms * 1e-3) / 1e9, 1)}
+        rec["roofline"]["traffic"] = None  # counters are taken on the plain windowed launch
     if cold is not None:
         rec["cold"] = cold
     if not args.no_cpu:
-        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.pool)
     print(json.dumps(rec), flush=True)
 
 
