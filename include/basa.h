@@ -116,6 +116,46 @@ int basa_window_attn_mem_fwd(const void* q, const void* k, const void* v, const 
                              int ww, int st, int sh, int sw, int head_dim, int dtype, hipStream_t stream);
 
 /*
+ * Window descriptors for true-window routing (paper §3.3 "Content-Adaptive True-Window
+ * Routing", its displayed equation): for every window m of the shifted partition,
+ *   qbar[b, h, m, :] = mean of q over the window's tokens, kbar likewise from k,
+ * accumulated in fp32. qbar, kbar: caller-owned fp32 device buffers [B, heads, n_win,
+ * head_dim], n_win = (T/wt)(H/wh)(W/ww), windows numbered as in basa_window_perm, 16-byte
+ * aligned, not overlapping q, k or each other. Grid/window/shift, dtype and errors as
+ * basa_window_attn_fwd.
+ */
+int basa_window_means(const void* q, const void* k, float* qbar, float* kbar, int B, int heads, int T, int H,
+                      int W, int wt, int wh, int ww, int st, int sh, int sw, int head_dim, int dtype,
+                      hipStream_t stream);
+
+/*
+ * Top-1 true-window routing (paper §3.3; App. A.2 "Video resolution extrapolation": one
+ * routed window, candidates within radius one). For window i of head (b, h):
+ *   route[b, h, i] = argmax over candidates j of qbar[b,h,i] . kbar[b,h,j] / sqrt(head_dim)
+ * where the candidates are the windows at Chebyshev distance 1 .. radius on the window
+ * grid (T/wt, H/wh, W/ww), without wrap-around and never i itself. Ties go to the lowest
+ * window index; a window without candidates gets -1. Scores are computed in fp32.
+ * qbar, kbar: fp32 device buffers as written by basa_window_means; route: caller-owned
+ * int32 device buffer [B, heads, n_win]. Errors: BASA_ERR_NULL, BASA_ERR_SHAPE (grid,
+ * window, radius < 0), BASA_ERR_UNSUPPORTED (head_dim), BASA_ERR_ALIGN, BASA_ERR_ALIAS.
+ */
+int basa_route_top1(const float* qbar, const float* kbar, int32_t* route, int B, int heads, int T, int H, int W,
+                    int wt, int wh, int ww, int radius, int head_dim, hipStream_t stream);
+
+/*
+ * Shifted window attention with a routed window and pooled memory (paper §3.3: the key
+ * and value source of window i is its own tokens, the routed windows' original tokens and
+ * the pooled memory). As basa_window_attn_mem_fwd, with route: optional (NULL = none)
+ * int32 device buffer [B, heads, n_win] (from basa_route_top1); when route[b, h, i] is a
+ * window index, the queries of window i also attend, in the same softmax, to that
+ * window's k/v tokens. Entries outside [0, n_win), such as -1, add nothing.
+ */
+int basa_window_attn_routed_fwd(const void* q, const void* k, const void* v, const int32_t* route,
+                                const void* kmem, const void* vmem, int n_mem, void* out, float* lse, int B,
+                                int heads, int T, int H, int W, int wt, int wh, int ww, int st, int sh, int sw,
+                                int head_dim, int dtype, hipStream_t stream);
+
+/*
  * Window membership export (paper §3.1): perm[m * Wtok + l] = flat original token of
  * local slot l of window m, Wtok = wt*wh*ww, windows numbered row-major over window
  * coordinates (t, h, w) and slots row-major over local coordinates (t, h, w). The table

@@ -10,10 +10,13 @@ from ._lib import (  # noqa: F401
     load,
     pool_kv,
     pooled_count,
+    route_top1,
     shift_schedule,
     status_string,
     version,
     window_attn_fwd,
     window_attn_mem_fwd,
+    window_attn_routed_fwd,
+    window_means,
     window_perm,
 )

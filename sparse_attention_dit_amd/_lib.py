@@ -18,7 +18,8 @@ DTYPE_BF16 = 1
 
 # Exported C symbols, in header order.
 SYMBOLS = ("basa_window_attn_fwd", "basa_full_attn_fwd", "basa_pool_kv", "basa_window_attn_mem_fwd",
-           "basa_window_perm", "basa_shift_schedule", "basa_status_string", "basa_version")
+           "basa_window_means", "basa_route_top1", "basa_window_attn_routed_fwd", "basa_window_perm",
+           "basa_shift_schedule", "basa_status_string", "basa_version")
 
 
 class BasaError(RuntimeError):
@@ -47,6 +48,12 @@ def load() -> ctypes.CDLL:
     lib.basa_pool_kv.restype = i
     lib.basa_window_attn_mem_fwd.argtypes = [vp] * 5 + [i, vp, vp] + [i] * 13 + [vp]
     lib.basa_window_attn_mem_fwd.restype = i
+    lib.basa_window_means.argtypes = [vp] * 4 + [i] * 13 + [vp]
+    lib.basa_window_means.restype = i
+    lib.basa_route_top1.argtypes = [vp] * 3 + [i] * 10 + [vp]
+    lib.basa_route_top1.restype = i
+    lib.basa_window_attn_routed_fwd.argtypes = [vp] * 6 + [i, vp, vp] + [i] * 13 + [vp]
+    lib.basa_window_attn_routed_fwd.restype = i
     lib.basa_window_perm.argtypes = [i] * 9 + [vp, vp]
     lib.basa_window_perm.restype = i
     lib.basa_shift_schedule.argtypes = [i] * 5 + [vp, vp]
@@ -152,6 +159,63 @@ def pool_kv(k, v, kmem, vmem, grid, pool, stream=None) -> None:
 def window_attn_mem_fwd(q, k, v, kmem, vmem, out, grid, window, shift, lse=None, stream=None) -> None:
     """Windowed attention whose keys/values are the window's plus the memory's (kmem,
     vmem: [B, heads, M, d]; None for no memory); lse: optional fp32 [B, heads, N]."""
+    window_attn_routed_fwd(q, k, v, None, kmem, vmem, out, grid, window, shift, lse, stream)
+
+
+def _n_win(grid, window):
+    (T, H, W), (wt, wh, ww) = ((int(x) for x in grid), (int(x) for x in window))
+    if min(T, H, W, wt, wh, ww) <= 0 or T % wt or H % wh or W % ww:
+        raise BasaError(2, f"window {window} does not divide grid {grid}")
+    return (T // wt) * (H // wh) * (W // ww)
+
+
+def window_means(q, k, qbar, kbar, grid, window, shift, stream=None) -> None:
+    """Window descriptors: qbar/kbar fp32 [B, heads, n_win, d] = means of q/k per window."""
+    import torch
+    if q.shape != k.shape or q.dtype != k.dtype or not (q.is_cuda and k.is_cuda) or q.dim() != 4:
+        raise BasaError(2, "q and k must be device tensors of one [B, heads, N, d] shape and dtype")
+    if not (q.is_contiguous() and k.is_contiguous()):
+        raise BasaError(2, "q and k must be contiguous")
+    B, H_, N, d = q.shape
+    want = (B, H_, _n_win(grid, window), d)
+    for name, t in (("qbar", qbar), ("kbar", kbar)):
+        if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != want:
+            raise BasaError(2, f"{name} must be a contiguous float32 device tensor {want}")
+    T, H, W = (int(x) for x in grid)
+    if T * H * W != N:
+        raise BasaError(2, f"grid {grid} holds {T * H * W} tokens, tensors hold {N}")
+    wt, wh, ww = (int(x) for x in window)
+    st, sh, sw = (int(x) for x in shift)
+    rc = load().basa_window_means(q.data_ptr(), k.data_ptr(), qbar.data_ptr(), kbar.data_ptr(), B, H_, T, H, W, wt,
+                                  wh, ww, st, sh, sw, d, _dtype_code(q), _stream_handle(stream))
+    if rc != 0:
+        raise BasaError(rc, "basa_window_means")
+
+
+def route_top1(qbar, kbar, route, grid, window, radius=1, stream=None) -> None:
+    """route int32 [B, heads, n_win]: best-scoring window within the radius (-1: none)."""
+    import torch
+    if qbar.shape != kbar.shape or qbar.dtype != torch.float32 or kbar.dtype != torch.float32 or qbar.dim() != 4:
+        raise BasaError(2, "qbar and kbar must be float32 [B, heads, n_win, d] of one shape")
+    B, H_, n_win, d = qbar.shape
+    if n_win != _n_win(grid, window):
+        raise BasaError(2, "descriptor count does not match the window grid")
+    if not route.is_cuda or route.dtype != torch.int32 or not route.is_contiguous() or tuple(route.shape) != (B, H_,
+                                                                                                               n_win):
+        raise BasaError(2, "route must be a contiguous int32 device tensor [B, heads, n_win]")
+    if not (qbar.is_cuda and kbar.is_cuda and qbar.is_contiguous() and kbar.is_contiguous()):
+        raise BasaError(2, "qbar and kbar must be contiguous device tensors")
+    T, H, W = (int(x) for x in grid)
+    wt, wh, ww = (int(x) for x in window)
+    rc = load().basa_route_top1(qbar.data_ptr(), kbar.data_ptr(), route.data_ptr(), B, H_, T, H, W, wt, wh, ww,
+                                int(radius), d, _stream_handle(stream))
+    if rc != 0:
+        raise BasaError(rc, "basa_route_top1")
+
+
+def window_attn_routed_fwd(q, k, v, route, kmem, vmem, out, grid, window, shift, lse=None, stream=None) -> None:
+    """Windowed attention over the window's, the routed window's (route int32 [B, heads,
+    n_win] or None) and the memory's keys/values (kmem, vmem or None); lse optional."""
     import torch
     _check_tensors(q, k, v, out)
     B, H_, N, d = q.shape
@@ -176,11 +240,17 @@ def window_attn_mem_fwd(q, k, v, kmem, vmem, out, grid, window, shift, lse=None,
         raise BasaError(2, f"grid {grid} holds {T * H * W} tokens, tensors hold {N}")
     wt, wh, ww = (int(x) for x in window)
     st, sh, sw = (int(x) for x in shift)
-    rc = load().basa_window_attn_mem_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), kp or None, vp_ or None, n_mem,
-                                         out.data_ptr(), lp or None, B, H_, T, H, W, wt, wh, ww, st, sh, sw, d,
-                                         _dtype_code(q), _stream_handle(stream))
+    rp = 0
+    if route is not None:
+        want = (B, H_, _n_win(grid, window))
+        if not route.is_cuda or route.dtype != torch.int32 or not route.is_contiguous() or tuple(route.shape) != want:
+            raise BasaError(2, f"route must be a contiguous int32 device tensor {want}")
+        rp = route.data_ptr()
+    rc = load().basa_window_attn_routed_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), rp or None, kp or None,
+                                            vp_ or None, n_mem, out.data_ptr(), lp or None, B, H_, T, H, W, wt, wh,
+                                            ww, st, sh, sw, d, _dtype_code(q), _stream_handle(stream))
     if rc != 0:
-        raise BasaError(rc, "basa_window_attn_mem_fwd")
+        raise BasaError(rc, "basa_window_attn_routed_fwd")
 
 
 def window_perm(grid, window, shift, perm, stream=None) -> None:

@@ -170,10 +170,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const uint32_t head_bytes = uint32_t(p.head_stride) * 2u;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + base, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + base, head_bytes);
-  // The key/value stream is the window's Tw tiles, then (§3.2) mem_tiles tiles of the
-  // pooled memory, a plain [n_mem, D] block per head.
+  // The key/value stream is the window's Tw tiles, then (§3.3) as many tiles of the routed
+  // window, if any, then (§3.2) mem_tiles tiles of the pooled memory, a plain [n_mem, D]
+  // block per head.
+  int32_t routed = p.route != nullptr ? p.route[int64_t(tile.bh) * p.n_win + tile.win] : -1;
+  if (routed < 0 || routed >= p.n_win) routed = -1;
+  const WinOrigin org_r = window_origin(p.map, uint32_t(routed < 0 ? 0 : routed));
   const int Tw = p.kv_tiles;
-  const int Tn = Tw + p.mem_tiles;
+  const int Tr = routed < 0 ? 0 : Tw;
+  const int Tn = Tw + Tr + p.mem_tiles;
   const int64_t mem_base = int64_t(tile.bh) * int64_t(p.n_mem) * D;
   const uint32_t mem_bytes = uint32_t(p.n_mem) * uint32_t(L::ROW_BYTES);
   const __amdgpu_buffer_rsrc_t kmrs = make_rsrc(static_cast<const uint16_t*>(p.kmem) + mem_base, mem_bytes);
@@ -193,11 +198,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // Byte offset of row r of key/value tile t (window tile, or memory tile past Tw).
   auto tile_row_offset = [&](int t, int r) __attribute__((always_inline)) -> uint32_t {
     if (t < Tw) return row_offset(t * BN + r);
-    const int j = (t - Tw) * BN + r;
+    if (t < Tw + Tr) {
+      const int local = (t - Tw) * BN + r;
+      return local < p.wtok ? uint32_t(token_of(p.map, org_r, uint32_t(local))) * uint32_t(L::ROW_BYTES)
+                            : 0xffffff00u;
+    }
+    const int j = (t - Tw - Tr) * BN + r;
     return j < p.n_mem ? uint32_t(j) * uint32_t(L::ROW_BYTES) : 0xffffff00u;
   };
   auto dma_tile = [&](const uint32_t* row_off, char* st, int t) __attribute__((always_inline)) {
-    const bool mem = t >= Tw;
+    const bool mem = t >= Tw + Tr;
     const __amdgpu_buffer_rsrc_t ks = mem ? kmrs : krs;
     const __amdgpu_buffer_rsrc_t vs = mem ? vmrs : vrs;
 #pragma unroll
@@ -309,8 +319,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       for (int kb = 0; kb < 2; ++kb)
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk][kb], qf[kk], sacc[kb], 0, 0, 0);
 
-    // ragged last tile of the window or of the memory: keys past the end get -inf
-    const int lim = t < Tw ? p.wtok - t * BN : p.n_mem - (t - Tw) * BN;
+    // ragged last tile of the window, the routed window or the memory: keys past the end
+    // get -inf
+    const int lim = t < Tw ? p.wtok - t * BN : t < Tw + Tr ? p.wtok - (t - Tw) * BN : p.n_mem - (t - Tw - Tr) * BN;
     if (lim < BN) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -459,14 +470,20 @@ __global__ __launch_bounds__(64) void win_attn_f32_kernel(const float* __restric
   float m = -__builtin_inff(), l = 0.0f;
   const float c = p.scale_log2;
 
-  // key/value tiles: the window's, then (§3.2) those of the pooled memory
+  // key/value tiles: the window's, the routed window's if any (§3.3), then those of the
+  // pooled memory (§3.2)
+  int32_t routed = p.route != nullptr ? p.route[int64_t(tile.bh) * p.n_win + tile.win] : -1;
+  if (routed < 0 || routed >= p.n_win) routed = -1;
+  const WinOrigin org_r = window_origin(p.map, uint32_t(routed < 0 ? 0 : routed));
   const int Tw = (p.wtok + BN - 1) / BN;
-  const int Tn = Tw + (p.n_mem + BN - 1) / BN;
+  const int Tr = routed < 0 ? 0 : Tw;
+  const int Tn = Tw + Tr + (p.n_mem + BN - 1) / BN;
   const float* kmem = static_cast<const float*>(p.kmem) + int64_t(tile.bh) * int64_t(p.n_mem) * D;
   const float* vmem = static_cast<const float*>(p.vmem) + int64_t(tile.bh) * int64_t(p.n_mem) * D;
   for (int t = 0; t < Tn; ++t) {
-    const bool mem = t >= Tw;
-    const int nrows = mem ? p.n_mem - (t - Tw) * BN : p.wtok - t * BN;
+    const bool mem = t >= Tw + Tr;
+    const bool rt = !mem && t >= Tw;
+    const int nrows = mem ? p.n_mem - (t - Tw - Tr) * BN : p.wtok - (rt ? t - Tw : t) * BN;
     __syncthreads();
     // 64 lanes load 32 rows: two lanes per row, each half of the row
     {
@@ -478,11 +495,12 @@ __global__ __launch_bounds__(64) void win_attn_f32_kernel(const float* __restric
         const float* ks;
         const float* vs;
         if (mem) {
-          const int64_t j = int64_t((t - Tw) * BN + r) * D + half * (D / 2);
+          const int64_t j = int64_t((t - Tw - Tr) * BN + r) * D + half * (D / 2);
           ks = kmem + j;
           vs = vmem + j;
         } else {
-          const int tok = token_of(p.map, org, uint32_t(t * BN + r));
+          const int tok = rt ? token_of(p.map, org_r, uint32_t((t - Tw) * BN + r))
+                             : token_of(p.map, org, uint32_t(t * BN + r));
           ks = k + base + int64_t(tok) * D + half * (D / 2);
           vs = v + base + int64_t(tok) * D + half * (D / 2);
         }
@@ -543,6 +561,127 @@ __global__ void win_perm_kernel(WinMap map, int32_t wtok, int32_t total, int32_t
   const int32_t win = idx / wtok;
   const int32_t local = idx - win * wtok;
   perm[idx] = token_of(map, window_origin(map, uint32_t(win)), uint32_t(local));
+}
+
+// ---------------------------------------------------------------------------------
+// Window descriptors (BASA §3.3): the mean of q (blockIdx.y = 0) or k (1) over each
+// window's members, in fp32. One workgroup per (bh, window): 256 threads take CPR chunks
+// of 256/CPR rows at a time (whole rows per group of CPR threads), then reduce the row
+// groups through LDS.
+template <int D, typename T>
+__global__ __launch_bounds__(256) void window_mean_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                          float* __restrict__ qbar, float* __restrict__ kbar,
+                                                          WinMap map, int32_t wtok, int32_t n_win,
+                                                          int64_t head_stride) {
+  constexpr int EPC = 16 / sizeof(T);
+  constexpr int CPR = D / EPC;
+  constexpr int RPP = 256 / CPR;  // rows per pass
+  __shared__ float part[RPP][D];
+  const T* src = blockIdx.y == 0 ? q : k;
+  float* dst = blockIdx.y == 0 ? qbar : kbar;
+  const int win = int(blockIdx.x % uint32_t(n_win));
+  const int64_t bh = blockIdx.x / uint32_t(n_win);
+  const WinOrigin org = window_origin(map, uint32_t(win));
+  const int chunk = threadIdx.x % CPR;
+  const int rsub = threadIdx.x / CPR;
+  const T* head = src + bh * head_stride + chunk * EPC;
+  float acc[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.0f;
+  for (int local = rsub; local < wtok; local += RPP) {
+    const T* row = head + int64_t(token_of(map, org, uint32_t(local))) * D;
+    if constexpr (sizeof(T) == 2) {
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(row);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += __uint_as_float(x[e] << 16);
+        acc[2 * e + 1] += __uint_as_float(x[e] & 0xffff0000u);
+      }
+    } else {
+      const float4 x = *reinterpret_cast<const float4*>(row);
+      acc[0] += x.x;
+      acc[1] += x.y;
+      acc[2] += x.z;
+      acc[3] += x.w;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) part[rsub][chunk * EPC + e] = acc[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float sum = 0.0f;
+    for (int r = 0; r < RPP; ++r) sum += part[r][threadIdx.x];
+    dst[(bh * n_win + win) * D + threadIdx.x] = sum / float(wtok);
+  }
+}
+
+// Top-1 routing over the radius neighbourhood of each window (BASA §3.3, App. A.2): one
+// thread per (bh, window); candidates in ascending index order, strict comparison, so
+// ties keep the lowest index.
+template <int D>
+__global__ __launch_bounds__(64) void route_top1_kernel(const float* __restrict__ qbar,
+                                                        const float* __restrict__ kbar, int32_t* __restrict__ route,
+                                                        int32_t bh_total, int32_t nt, int32_t nh, int32_t nw,
+                                                        int32_t radius, float scale) {
+  const int64_t idx = int64_t(blockIdx.x) * 64 + threadIdx.x;
+  const int64_t n_win = int64_t(nt) * nh * nw;
+  if (idx >= int64_t(bh_total) * n_win) return;
+  const int64_t bh = idx / n_win;
+  const int i = int(idx % n_win);
+  const int ti = i / (nh * nw), hi = (i / nw) % nh, wi = i % nw;
+  const float* qi = qbar + idx * D;
+  int best = -1;
+  float best_s = 0.0f;
+  for (int tj = max(0, ti - radius); tj <= min(nt - 1, ti + radius); ++tj)
+    for (int hj = max(0, hi - radius); hj <= min(nh - 1, hi + radius); ++hj)
+      for (int wj = max(0, wi - radius); wj <= min(nw - 1, wi + radius); ++wj) {
+        const int j = (tj * nh + hj) * nw + wj;
+        if (j == i) continue;
+        const float* kj = kbar + (bh * n_win + j) * D;
+        float s = 0.0f;
+        for (int d = 0; d < D; ++d) s = __builtin_fmaf(qi[d], kj[d], s);
+        s *= scale;
+        if (best < 0 || s > best_s) {
+          best = j;
+          best_s = s;
+        }
+      }
+  route[idx] = best;
+}
+
+hipError_t launch_window_means(const void* q, const void* k, float* qbar, float* kbar, const WinMap& map,
+                               int32_t wtok, int32_t n_win, int32_t bh, int64_t head_stride, int head_dim, bool bf16,
+                               hipStream_t stream) {
+  const uint64_t blocks = uint64_t(bh) * uint64_t(n_win);
+  if (blocks == 0 || blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
+  const dim3 grid(uint32_t(blocks), 2);
+#define BASA_MEANS(DD, TT)                                                                                      \
+  hipLaunchKernelGGL((window_mean_kernel<DD, TT>), grid, dim3(256), 0, stream, static_cast<const TT*>(q),      \
+                     static_cast<const TT*>(k), qbar, kbar, map, wtok, n_win, head_stride)
+  if (bf16 && head_dim == 128) BASA_MEANS(128, uint16_t);
+  else if (bf16 && head_dim == 64) BASA_MEANS(64, uint16_t);
+  else if (!bf16 && head_dim == 128) BASA_MEANS(128, float);
+  else if (!bf16 && head_dim == 64) BASA_MEANS(64, float);
+  else return hipErrorInvalidValue;
+#undef BASA_MEANS
+  return hipGetLastError();
+}
+
+hipError_t launch_route_top1(const float* qbar, const float* kbar, int32_t* route, int32_t bh, int32_t nt,
+                             int32_t nh, int32_t nw, int32_t radius, int head_dim, hipStream_t stream) {
+  const uint64_t threads = uint64_t(bh) * uint64_t(nt) * uint64_t(nh) * uint64_t(nw);
+  const uint64_t blocks = (threads + 63) / 64;
+  if (blocks == 0 || blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
+  const float scale = float(1.0 / sqrt(double(head_dim)));
+  if (head_dim == 128)
+    hipLaunchKernelGGL(route_top1_kernel<128>, dim3(uint32_t(blocks)), dim3(64), 0, stream, qbar, kbar, route, bh,
+                       nt, nh, nw, radius, scale);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL(route_top1_kernel<64>, dim3(uint32_t(blocks)), dim3(64), 0, stream, qbar, kbar, route, bh,
+                       nt, nh, nw, radius, scale);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------

@@ -27,12 +27,25 @@ struct AttnParams {
   int32_t mem_tiles;
   float* lse;           // optional [B*heads, N] natural-log log-sum-exp of each row's logits
   int32_t n_tokens;     // N
+  // optional routed window per (batch*head, window) (§3.3): its tokens follow the window's
+  // own in the key/value stream; -1 (or any value outside [0, n_win)) routes nothing
+  const int32_t* route;
 };
 
 hipError_t launch_window_attention(const void* q, const void* k, const void* v, void* out, const AttnParams& p,
                                    int head_dim, bool bf16, hipStream_t stream);
 
 hipError_t launch_window_perm(const WinMap& map, int32_t wtok, int32_t total, int32_t* perm, hipStream_t stream);
+
+// Window descriptors (§3.3): qbar/kbar [BH, n_win, D] fp32 = means of q/k over each window.
+hipError_t launch_window_means(const void* q, const void* k, float* qbar, float* kbar, const WinMap& map,
+                               int32_t wtok, int32_t n_win, int32_t bh, int64_t head_stride, int head_dim, bool bf16,
+                               hipStream_t stream);
+
+// Top-1 routing (§3.3): route[bh, i] = argmax over windows j at Chebyshev distance 1..radius
+// of qbar[bh,i] . kbar[bh,j] / sqrt(D) (lowest j on ties, -1 without candidates).
+hipError_t launch_route_top1(const float* qbar, const float* kbar, int32_t* route, int32_t bh, int32_t nt,
+                             int32_t nh, int32_t nw, int32_t radius, int head_dim, hipStream_t stream);
 
 // Pooled memory: kmem/vmem [BH, T*gh*gw, D] = means of k/v over ph x pw regions per frame.
 hipError_t launch_pool_kv(const void* k, const void* v, void* kmem, void* vmem, int32_t bh, int32_t T, int32_t H,

@@ -39,10 +39,11 @@ int check_grid(int T, int H, int W, int wt, int wh, int ww) {
   return BASA_OK;
 }
 
-// Memory (kmem, vmem, n_mem) and lse are optional: n_mem = 0 with null kmem/vmem, lse null.
-int run_attention(const void* q, const void* k, const void* v, const void* kmem, const void* vmem, int n_mem,
-                  void* out, float* lse, int B, int heads, int T, int H, int W, int wt, int wh, int ww, int st,
-                  int sh, int sw, int head_dim, int dtype, hipStream_t stream) {
+// Memory (kmem, vmem, n_mem), lse and route are optional: n_mem = 0 with null kmem/vmem,
+// null lse, null route.
+int run_attention(const void* q, const void* k, const void* v, const int32_t* route, const void* kmem,
+                  const void* vmem, int n_mem, void* out, float* lse, int B, int heads, int T, int H, int W, int wt,
+                  int wh, int ww, int st, int sh, int sw, int head_dim, int dtype, hipStream_t stream) {
   if (!q || !k || !v || !out) return BASA_ERR_NULL;
   if (n_mem < 0) return BASA_ERR_SHAPE;
   if (n_mem > 0 && (!kmem || !vmem)) return BASA_ERR_NULL;
@@ -63,6 +64,7 @@ int run_attention(const void* q, const void* k, const void* v, const void* kmem,
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return BASA_ERR_ALIGN;
   if (n_mem > 0 && (!aligned(kmem, 16) || !aligned(vmem, 16))) return BASA_ERR_ALIGN;
   if (lse && !aligned(lse, 4)) return BASA_ERR_ALIGN;
+  if (route && !aligned(route, 4)) return BASA_ERR_ALIGN;
   const int64_t elem = dtype == BASA_DTYPE_BF16 ? 2 : 4;
   const int64_t bytes = bh * N * head_dim * elem;
   const int64_t mem_bytes = bh * int64_t(n_mem) * head_dim * elem;
@@ -93,6 +95,7 @@ int run_attention(const void* q, const void* k, const void* v, const void* kmem,
   p.mem_tiles = 0;
   p.lse = lse;
   p.n_tokens = int32_t(N);
+  p.route = route;
   const hipError_t e =
       basa::launch_window_attention(q, k, v, out, p, head_dim, dtype == BASA_DTYPE_BF16, stream);
   if (e == hipErrorInvalidConfiguration) return BASA_ERR_OVERFLOW;
@@ -106,21 +109,77 @@ extern "C" {
 int basa_window_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int heads, int T, int H,
                          int W, int wt, int wh, int ww, int st, int sh, int sw, int head_dim, int dtype,
                          hipStream_t stream) {
-  return run_attention(q, k, v, nullptr, nullptr, 0, out, nullptr, B, heads, T, H, W, wt, wh, ww, st, sh, sw,
-                       head_dim, dtype, stream);
+  return run_attention(q, k, v, nullptr, nullptr, nullptr, 0, out, nullptr, B, heads, T, H, W, wt, wh, ww, st, sh,
+                       sw, head_dim, dtype, stream);
 }
 
 int basa_full_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int heads, int N,
                        int head_dim, int dtype, hipStream_t stream) {
-  return run_attention(q, k, v, nullptr, nullptr, 0, out, nullptr, B, heads, 1, 1, N, 1, 1, N, 0, 0, 0, head_dim,
-                       dtype, stream);
+  return run_attention(q, k, v, nullptr, nullptr, nullptr, 0, out, nullptr, B, heads, 1, 1, N, 1, 1, N, 0, 0, 0,
+                       head_dim, dtype, stream);
 }
 
 int basa_window_attn_mem_fwd(const void* q, const void* k, const void* v, const void* kmem, const void* vmem,
                              int n_mem, void* out, float* lse, int B, int heads, int T, int H, int W, int wt, int wh,
                              int ww, int st, int sh, int sw, int head_dim, int dtype, hipStream_t stream) {
-  return run_attention(q, k, v, kmem, vmem, n_mem, out, lse, B, heads, T, H, W, wt, wh, ww, st, sh, sw, head_dim,
-                       dtype, stream);
+  return run_attention(q, k, v, nullptr, kmem, vmem, n_mem, out, lse, B, heads, T, H, W, wt, wh, ww, st, sh, sw,
+                       head_dim, dtype, stream);
+}
+
+int basa_window_attn_routed_fwd(const void* q, const void* k, const void* v, const int32_t* route, const void* kmem,
+                                const void* vmem, int n_mem, void* out, float* lse, int B, int heads, int T, int H,
+                                int W, int wt, int wh, int ww, int st, int sh, int sw, int head_dim, int dtype,
+                                hipStream_t stream) {
+  return run_attention(q, k, v, route, kmem, vmem, n_mem, out, lse, B, heads, T, H, W, wt, wh, ww, st, sh, sw,
+                       head_dim, dtype, stream);
+}
+
+int basa_window_means(const void* q, const void* k, float* qbar, float* kbar, int B, int heads, int T, int H, int W,
+                      int wt, int wh, int ww, int st, int sh, int sw, int head_dim, int dtype, hipStream_t stream) {
+  if (!q || !k || !qbar || !kbar) return BASA_ERR_NULL;
+  if (dtype != BASA_DTYPE_F32 && dtype != BASA_DTYPE_BF16) return BASA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return BASA_ERR_UNSUPPORTED;
+  if (B <= 0 || heads <= 0) return BASA_ERR_SHAPE;
+  const int g = check_grid(T, H, W, wt, wh, ww);
+  if (g != BASA_OK) return g;
+  const int64_t N = int64_t(T) * H * W;
+  const int64_t bh = int64_t(B) * heads;
+  if (bh > kInt32Max || N * head_dim > kInt32Max) return BASA_ERR_OVERFLOW;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(qbar, 16) || !aligned(kbar, 16)) return BASA_ERR_ALIGN;
+  const int64_t wtok = int64_t(wt) * wh * ww;
+  const int64_t n_win = N / wtok;
+  const int64_t elem = dtype == BASA_DTYPE_BF16 ? 2 : 4;
+  const int64_t in_bytes = bh * N * head_dim * elem, out_bytes = bh * n_win * head_dim * 4;
+  if (overlaps2(qbar, out_bytes, q, in_bytes) || overlaps2(qbar, out_bytes, k, in_bytes) ||
+      overlaps2(kbar, out_bytes, q, in_bytes) || overlaps2(kbar, out_bytes, k, in_bytes) ||
+      overlaps2(qbar, out_bytes, kbar, out_bytes))
+    return BASA_ERR_ALIAS;
+  const basa::WinMap map =
+      basa::make_winmap(T, H, W, wt, wh, ww, reduce_mod(st, T), reduce_mod(sh, H), reduce_mod(sw, W));
+  const hipError_t e = basa::launch_window_means(q, k, qbar, kbar, map, int32_t(wtok), int32_t(n_win), int32_t(bh),
+                                                 N * head_dim, head_dim, dtype == BASA_DTYPE_BF16, stream);
+  if (e == hipErrorInvalidConfiguration) return BASA_ERR_OVERFLOW;
+  return e == hipSuccess ? BASA_OK : BASA_ERR_HIP;
+}
+
+int basa_route_top1(const float* qbar, const float* kbar, int32_t* route, int B, int heads, int T, int H, int W,
+                    int wt, int wh, int ww, int radius, int head_dim, hipStream_t stream) {
+  if (!qbar || !kbar || !route) return BASA_ERR_NULL;
+  if (head_dim != 64 && head_dim != 128) return BASA_ERR_UNSUPPORTED;
+  if (B <= 0 || heads <= 0 || radius < 0) return BASA_ERR_SHAPE;
+  const int g = check_grid(T, H, W, wt, wh, ww);
+  if (g != BASA_OK) return g;
+  const int64_t bh = int64_t(B) * heads;
+  if (bh > kInt32Max) return BASA_ERR_OVERFLOW;
+  if (!aligned(qbar, 4) || !aligned(kbar, 4) || !aligned(route, 4)) return BASA_ERR_ALIGN;
+  const int64_t n_win = int64_t(T / wt) * (H / wh) * (W / ww);
+  const int64_t desc_bytes = bh * n_win * head_dim * 4, route_bytes = bh * n_win * 4;
+  if (overlaps2(route, route_bytes, qbar, desc_bytes) || overlaps2(route, route_bytes, kbar, desc_bytes))
+    return BASA_ERR_ALIAS;
+  const hipError_t e = basa::launch_route_top1(qbar, kbar, route, int32_t(bh), T / wt, H / wh, W / ww, radius,
+                                               head_dim, stream);
+  if (e == hipErrorInvalidConfiguration) return BASA_ERR_OVERFLOW;
+  return e == hipSuccess ? BASA_OK : BASA_ERR_HIP;
 }
 
 int basa_pool_kv(const void* k, const void* v, void* kmem, void* vmem, int B, int heads, int T, int H, int W,
@@ -173,7 +232,7 @@ const char* basa_status_string(int status) {
   }
 }
 
-int basa_version(void) { return (1 << 16) | 2; }
+int basa_version(void) { return (1 << 16) | 3; }
 
 // Interleaved shift schedule, BASA §3.1: per axis the offsets (i * delta) mod w with
 // delta = max(1, floor(w / L)) are taken alternately from their first ceil(L/2) and the

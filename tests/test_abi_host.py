@@ -114,6 +114,36 @@ def test_memory_and_pool_argument_errors():
     assert pool(km=A) == 4 and pool(vm=E) == 4
 
 
+def test_routing_argument_errors():
+    """The routing entry points through the Python binding's own argument lists (so a
+    binding/signature mismatch fails here too) and the raw ABI."""
+    lib = _lib.load()
+    E, F, G = 0x50000000, 0x60000000, 0x70000000
+
+    def means(q=A, k=Bp, qb=E, kb=F, d=128, dtype=1, window=(1, 8, 8)):
+        return lib.basa_window_means(q, k, qb, kb, 1, 2, 1, 16, 16, *window, 0, 4, 4, d, dtype, None)
+    assert means(q=None) == 1 and means(kb=None) == 1
+    assert means(window=(1, 5, 8)) == 2
+    assert means(d=80) == 3 and means(dtype=7) == 3
+    assert means(qb=E + 4) == 7
+    assert means(qb=A) == 4 and means(kb=E) == 4
+
+    def route(qb=E, kb=F, r=G, radius=1, d=128):
+        return lib.basa_route_top1(qb, kb, r, 1, 2, 1, 16, 16, 1, 8, 8, radius, d, None)
+    assert route(r=None) == 1
+    assert route(radius=-1) == 2
+    assert route(d=32) == 3
+    assert route(r=G + 2) == 7
+    assert route(r=E) == 4
+
+    def routed(rt=G, km=None, vm=None, n_mem=0, lse=None):
+        return lib.basa_window_attn_routed_fwd(A, Bp, Cp, rt, km, vm, n_mem, D, lse, 1, 2, 1, 16, 16, 1, 8, 8, 0, 4, 4,
+                                               128, 1, None)
+    assert routed(rt=G + 2) == 7
+    assert routed(n_mem=4) == 1
+    assert routed(lse=D) == 4
+
+
 @pytest.fixture(scope="module")
 def index_tool(tmp_path_factory):
     exe = str(tmp_path_factory.mktemp("idx") / "index_map_check")
