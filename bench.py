@@ -8,7 +8,7 @@ protocol (§4 / App. A.2 "Implementation and latency measurement"): warm-up firs
 events around the timed region, synchronisation before reading them.
 
 Prints ONE JSON line (rank 0). Usage:
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--cold] [--pool P]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--cold] [--pool P] [--route]
 """
 from __future__ import annotations
 
@@ -47,13 +47,14 @@ def measured_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, min_s: float, pool: int = 0):
+def cpu_baseline(w, min_s: float, pool: int = 0, route: bool = False):
     """Time the fp64 oracle (as it stands) on a bounded sample of the workload: whole
     (shift, head) slices of the windowed attention (with pooled memory when pool > 0; the
     pooling itself is done once, untimed), in step order and cycling, until at least min_s
     of CPU work."""
     from oracle import basa_oracle as O
     from oracle import memory_oracle as MO
+    from oracle import routing_oracle as RO
     from sparse_attention_dit_amd import inputs
     try:
         from threadpoolctl import threadpool_info
@@ -63,20 +64,29 @@ def cpu_baseline(w, min_s: float, pool: int = 0):
     t = inputs.draw_qkv((w.batch, 1, w.tokens, w.head_dim), w.dtype, seed=w.seed)
     q, k, v = (t.exact[n] for n in "qkv")
     n_mem = 0
+    km = vm = None
     if pool:
         km, vm = MO.pool_kv(k, w.grid, (pool, pool)), MO.pool_kv(v, w.grid, (pool, pool))
         n_mem = km.shape[2]
-    slices, elapsed = 0, 0.0
+    routes = {}
+    if route:  # routing decisions per shift, outside the timed region
+        for s in w.shifts:
+            routes[s] = RO.route_top1(RO.window_means(q, w.grid, w.window, s), RO.window_means(k, w.grid, w.window, s),
+                                      w.grid, w.window)
+    slices, elapsed, keys = 0, 0.0, 0.0
     while elapsed < min_s:
         shift = w.shifts[(slices // w.heads) % len(w.shifts)]
         t0 = time.perf_counter()
-        if pool:
+        if route:
+            RO.routed_attention(q, k, v, routes[shift], w.grid, w.window, shift, km, vm)
+        elif pool:
             MO.window_attention_memory(q, k, v, km, vm, w.grid, w.window, shift)
         else:
             O.window_attention(q, k, v, w.grid, w.window, shift)
         elapsed += time.perf_counter() - t0
         slices += 1
-    flops = 4 * w.batch * slices * w.tokens * (w.window_tokens + n_mem) * w.head_dim
+        keys += w.window_tokens * (1.0 + (float((routes[shift] >= 0).mean()) if route else 0.0)) + n_mem
+    flops = 4 * w.batch * w.tokens * keys * w.head_dim
     return {
         "value": flops / elapsed / 1e12,
         "unit": "TFLOP/s",
@@ -100,6 +110,7 @@ def main():
     ap.add_argument("--cold", action="store_true", help="also time HBM-cold launches (L2/MALL flushed between)")
     ap.add_argument("--pool", type=int, default=0,
                     help="with pooled global memory of p x p regions (0: plain windowed attention)")
+    ap.add_argument("--route", action="store_true", help="with top-1 true-window routing (radius one)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU work timed for cpu_baseline")
     args = ap.parse_args()
 
@@ -125,6 +136,14 @@ def main():
     out = torch.empty_like(dev["q"])
     stream = torch.cuda.current_stream()
     n_mem = 0
+    routed_frac = 0.0
+    if args.route:
+        # true-window routing (§3.3): per shift, window descriptors, top-1 routing within
+        # radius one, then attention over window + routed window (+ memory with --pool)
+        n_win = w.num_windows
+        qbar = torch.empty((w.batch, w.heads, n_win, w.head_dim), dtype=torch.float32, device="cuda")
+        kbar = torch.empty_like(qbar)
+        routes = [torch.empty((w.batch, w.heads, n_win), dtype=torch.int32, device="cuda") for _ in w.shifts]
     if args.pool:
         # K/V-pooled global memory (§3.2): pooled once per step (it does not depend on the
         # shift), then every shift's windows attend to window + memory keys
@@ -133,11 +152,22 @@ def main():
         kmem = torch.empty((w.batch, w.heads, n_mem, w.head_dim), dtype=dev["k"].dtype, device="cuda")
         vmem = torch.empty_like(kmem)
 
+    if args.pool or args.route:
+        km_ = kmem if args.pool else None
+        vm_ = vmem if args.pool else None
+
+        def attend(i, s):
+            if args.route:
+                _lib.window_means(dev["q"], dev["k"], qbar, kbar, w.grid, w.window, s, stream)
+                _lib.route_top1(qbar, kbar, routes[i], w.grid, w.window, 1, stream)
+            _lib.window_attn_routed_fwd(dev["q"], dev["k"], dev["v"], routes[i] if args.route else None, km_, vm_,
+                                        out, w.grid, w.window, s, stream=stream)
+
         def step():
-            _lib.pool_kv(dev["k"], dev["v"], kmem, vmem, w.grid, pool, stream)
-            for s in w.shifts:
-                _lib.window_attn_mem_fwd(dev["q"], dev["k"], dev["v"], kmem, vmem, out, w.grid, w.window, s,
-                                         stream=stream)
+            if args.pool:
+                _lib.pool_kv(dev["k"], dev["v"], kmem, vmem, w.grid, pool, stream)
+            for i, s in enumerate(w.shifts):
+                attend(i, s)
     else:
         def step():
             for s in w.shifts:
@@ -176,9 +206,8 @@ def main():
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(args.steps):
-            if args.pool:
-                _lib.window_attn_mem_fwd(dev["q"], dev["k"], dev["v"], kmem, vmem, out, w.grid, w.window, s,
-                                         stream=stream)
+            if args.pool or args.route:
+                attend(w.shifts.index(s), s)
             else:
                 _lib.window_attn_fwd(dev["q"], dev["k"], dev["v"], out, w.grid, w.window, s, stream)
         e1.record(stream)
@@ -228,12 +257,17 @@ def main():
     torch.cuda.synchronize()
     ms_full = fs.elapsed_time(fe) / args.full_iters
 
-    # attention FLOPs per launch: 4*B*h*N*(W + M)*d, M = memory tokens (0 without --pool);
-    # with --pool a "launch" is one shift's attention plus its share of the pooling
-    flops_launch = 4 * w.batch * w.heads * w.tokens * (w.window_tokens + n_mem) * w.head_dim
+    # attention FLOPs per launch: 4*B*h*N*(W*(1 + r) + M)*d, M = memory tokens (0 without
+    # --pool), r = fraction of windows with a routed window (0 without --route); with
+    # --pool/--route a "launch" is one shift's attention plus its share of the pooling and
+    # its routing
+    if args.route:
+        routed_frac = float(sum((r >= 0).float().mean().item() for r in routes) / len(routes))
+    keys_per_query = w.window_tokens * (1.0 + routed_frac) + n_mem
+    flops_launch = 4 * w.batch * w.heads * w.tokens * keys_per_query * w.head_dim
     tflops = flops_launch / (ms_per_launch * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
-    theoretical = w.tokens / (w.window_tokens + n_mem)
+    theoretical = w.tokens / keys_per_query
     measured = ms_full / ms_per_launch
     io_gbs = w.io_bytes() / (ms_per_launch * 1e-3) / 1e9
 
@@ -271,11 +305,14 @@ def main():
         rec["config"]["memory_tokens"] = n_mem
         rec["pool"] = {"pool_ms": round(pool_ms, 4),
                        "pool_gbs": round((w.io_bytes() // 2 + G_bytes) / (pool_ms * 1e-3) / 1e9, 1)}
+    if args.route:
+        rec["config"]["route"] = {"k": 1, "radius": 1, "routed_fraction": round(routed_frac, 4)}
+    if args.pool or args.route:
         rec["roofline"]["traffic"] = None  # counters are taken on the plain windowed launch
     if cold is not None:
         rec["cold"] = cold
     if not args.no_cpu:
-        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.pool)
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.pool, args.route)
     print(json.dumps(rec), flush=True)
 
 
