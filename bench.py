@@ -34,6 +34,53 @@ PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "flux-2048-128x128-w32"
 
 
+class ClockSampler:
+    """Samples the GPU core clock (the current level of the amdgpu driver's pp_dpm_sclk file)
+    every `period` seconds on a background thread. Only used when exactly one card is
+    visible; otherwise reports nothing. Reading the file does not touch the GPU queues."""
+
+    def __init__(self, period: float = 0.01):
+        import glob
+        import threading
+        files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = files[0] if len(files) == 1 else None
+        self.period = period
+        self.samples = []  # (perf_counter time, MHz)
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True) if self.path else None
+
+    def _read(self):
+        try:
+            with open(self.path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return float(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            mhz = self._read()
+            if mhz is not None:
+                self.samples.append((time.perf_counter(), mhz))
+            time.sleep(self.period)
+
+    def start(self):
+        if self._thread:
+            self._thread.start()
+        return self
+
+    def stop(self):
+        if self._thread:
+            self._stop.set()
+            self._thread.join()
+
+    def median(self, t0: float, t1: float):
+        vals = sorted(m for t, m in self.samples if t0 <= t <= t1)
+        return None if not vals else vals[len(vals) // 2], len(vals)
+
+
 def measured_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary of this
     workload, if it was taken on the current kernel sources; else None."""
@@ -176,6 +223,7 @@ def main():
     # The GPU's clocks need tens of milliseconds of sustained work to ramp up: before the W
     # warm-up steps, run untimed steps for ~0.5 s (sized from one step), reported as
     # "clock_settle_steps".
+    clock = ClockSampler().start()
     settle = 0
     if args.settle_s > 0:
         step()
@@ -189,12 +237,17 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    t_timed = time.perf_counter()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for _ in range(args.steps):
         step()
     end.record(stream)
     torch.cuda.synchronize()
+    clock.stop()
+    # the timed region is short; the clock is taken over it and the last 0.25 s before it,
+    # spent on the same steps
+    sclk_mhz, sclk_samples = clock.median(t_timed - 0.25, time.perf_counter())
     ms_total = start.elapsed_time(end)
     ms_per_step = ms_total / args.steps
     launches = args.steps * len(w.shifts)
@@ -297,6 +350,11 @@ def main():
                     "full_attn_tflops": round(w.full_flops() / (ms_full * 1e-3) / 1e12, 2)},
         "per_shift_ms": per_shift_ms,
         "io_gbs": round(io_gbs, 1),
+        # The core clock under this load: the chip is power-limited, so it runs below the
+        # 2.4 GHz the peak assumes; frac_at_clock is achieved / (peak * sclk / 2400).
+        "sclk_mhz": None if sclk_mhz is None else {
+            "median": sclk_mhz, "samples": sclk_samples, "source": "pp_dpm_sclk",
+            "frac_at_clock": round(tflops / (peak * sclk_mhz / 2400.0), 4)},
         "kernel_hash": kernel_hash(),
     }
     if args.pool:

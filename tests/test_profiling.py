@@ -82,3 +82,23 @@ def test_committed_traffic_records_are_consistent():
         assert name == profiling.traffic_json_name(wl.name)
         assert rec["algorithmic_bytes_per_launch"] == wl.io_bytes()
         assert rec["hbm_bytes_per_launch"] == rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+
+
+def test_clock_sampler_reads_the_marked_level(tmp_path):
+    """bench.py's clock sampler takes the level marked '*' in the driver's pp_dpm_sclk text
+    (idle: the sleep level; under load: the current frequency between min and max)."""
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    s = bench.ClockSampler()
+    f = tmp_path / "pp_dpm_sclk"
+    s.path = str(f)
+    f.write_text("0: 500Mhz\n1: 1916Mhz *\n2: 2400Mhz\n")
+    assert s._read() == 1916.0
+    f.write_text("S: 111Mhz *\n0: 500Mhz\n1: 2400Mhz\n")
+    assert s._read() == 111.0
+    f.write_text("0: 500Mhz\n1: 2400Mhz\n")
+    assert s._read() is None
+    s.samples = [(0.0, 1900.0), (1.0, 1950.0), (2.0, 1920.0), (3.0, 2400.0)]
+    assert s.median(0.5, 2.5) == (1950.0, 2)
+    assert s.median(5.0, 6.0) == (None, 0)
