@@ -140,11 +140,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // Device-only builtins are called through __device__ functions: called directly from a
 // lambda inside a kernel template, the buffer-to-LDS builtin can make hipcc's host pass
 // drop the kernel's launch stub without a diagnostic.
+// cache-policy operand of the buffer intrinsics: NT (non-temporal, streaming) on gfx950
+constexpr int kCachePolicyNT = 2;
+template <int CPOL = 0>
 __device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t rs, char* dst, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)dst, 16, off, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)dst, 16, off, 0, 0, CPOL);
 }
+// Output rows are written once and not read again by this kernel: non-temporal stores
+// (cache policy NT) keep them from displacing the window's K/V in L2, which the window's
+// other query tiles still read.
 __device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t rs, uint32_t off, u32x4_t x) {
-  __builtin_amdgcn_raw_buffer_store_b128(x, rs, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(x, rs, off, 0, kCachePolicyNT);
 }
 
 template <int D, int NW>
@@ -252,6 +258,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   // ---- Q: each wave DMAs its own 32 rows into the Q buffer (laid out like a K tile, 4 whole
   // rows per wave-wide load), and after the prologue barrier reads its fragments from there.
+  // Q is read once per workgroup: non-temporal loads keep it out of the way of the K/V in L2.
   // qrowtab keeps the byte offset of every query row for the output stores.
   constexpr int QG = 32 / RPG;  // row groups per wave
   __shared__ __attribute__((aligned(1024))) char qbuf[NW * QG * RG];
@@ -261,7 +268,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int i = 0; i < QG; ++i) {
       const int g = wave * QG + i;
-      dma16_to_lds(qrs, qbuf + g * RG, row_offset(tile.qtile * BM + g * RPG + ld_row) + k_chunk_off);
+      dma16_to_lds<kCachePolicyNT>(qrs, qbuf + g * RG, row_offset(tile.qtile * BM + g * RPG + ld_row) + k_chunk_off);
     }
     if (tid < BM) qrowtab[tid] = row_offset(tile.qtile * BM + tid);
   }
