@@ -109,6 +109,11 @@ struct TileLayout {
   static constexpr int CS = RPG * 16;                // chunk-slot stride inside a group
   static constexpr int RG = 1024 + CS;               // group stride
   __host__ __device__ static constexpr int v_slot(int c) { return c >= CPR / 2 ? (c ^ (D == 128 ? 2 : 1)) : c; }
+  // D = 64: in V, the upper-half chunks of row r of a group are stored at row position r ^ 4,
+  // so a transpose read of rows 0-3 touches the lower half's bytes 0-63 and the upper half's
+  // bytes 64-127 of their slots: with the neighbour swap, the four chunks of one half-wave's
+  // read then cover the 64 banks once.
+  static constexpr bool V_ROW_SWIZZLE = D == 64;
 };
 
 template <int D, int NW>
@@ -202,6 +207,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int ld_row = lane % RPG;
   const uint32_t k_chunk_off = uint32_t(ld_slot) * 16u;
   const uint32_t v_chunk_off = uint32_t(L::v_slot(ld_slot)) * 16u;
+  // row of its group that the lane loads for V (differs from ld_row only for the upper-half
+  // chunks of D = 64; see TileLayout)
+  const int v_ld_row = (L::V_ROW_SWIZZLE && ld_slot >= CPR / 2) ? (ld_row ^ 4) : ld_row;
   // Byte offset of a window row in the head (rows past the window get an offset beyond the
   // buffer range, so they read as zeros).
   auto row_offset = [&](int local) __attribute__((always_inline)) -> uint32_t {
@@ -218,6 +226,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int j = (t - Tw - Tr) * BN + r;
     return j < p.n_mem ? uint32_t(j) * uint32_t(L::ROW_BYTES) : 0xffffff00u;
   };
+  // row_off: LOADS byte offsets of the lane's K rows, then LOADS of its V rows
   auto dma_tile = [&](const uint32_t* row_off, char* st, int t) __attribute__((always_inline)) {
     const bool mem = t >= Tw + Tr;
     const __amdgpu_buffer_rsrc_t ks = mem ? kmrs : krs;
@@ -226,7 +235,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int i = 0; i < C::LOADS; ++i) {
       const int g = wave * C::LOADS + i;
       dma16_to_lds(ks, st + g * RG, row_off[i] + k_chunk_off);
-      dma16_to_lds(vs, st + C::TILE_BYTES + g * RG, row_off[i] + v_chunk_off);
+      dma16_to_lds(vs, st + C::TILE_BYTES + g * RG, row_off[C::LOADS + i] + v_chunk_off);
     }
   };
   // The row offsets of the K/V tiles are computed cooperatively a few tiles ahead into a
@@ -244,14 +253,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   };
   auto read_offs = [&](int t, uint32_t* row_off) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i)
+    for (int i = 0; i < C::LOADS; ++i) {
       row_off[i] = rowtab[(t % TAB_TILES) * BN + (wave * C::LOADS + i) * RPG + ld_row];
+      if constexpr (L::V_ROW_SWIZZLE)
+        row_off[C::LOADS + i] = rowtab[(t % TAB_TILES) * BN + (wave * C::LOADS + i) * RPG + v_ld_row];
+      else
+        row_off[C::LOADS + i] = row_off[i];
+    }
   };
 
   {  // tile 0 straight from the index map, the table for tiles 0 .. TAB_TILES - 1
-    uint32_t off0[C::LOADS];
+    uint32_t off0[2 * C::LOADS];
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) off0[i] = row_offset((wave * C::LOADS + i) * RPG + ld_row);
+    for (int i = 0; i < C::LOADS; ++i) {
+      off0[i] = row_offset((wave * C::LOADS + i) * RPG + ld_row);
+      off0[C::LOADS + i] = row_offset((wave * C::LOADS + i) * RPG + v_ld_row);
+    }
     dma_tile(off0, stage0, 0);
   }
   fill_tab(0, min(TAB_TILES, Tn));
@@ -288,12 +305,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int vg = l32 >> 4;
   const int vi = lane & 15;
   const int v_chunk = ((vi & 1) ? CPR / 2 : 0) + vg;           // + 2*db per block
-  // per d block: the slot of chunk v_chunk + 2*db, less the 2*db*CS added at each read
-  int v_rd[DB];
+  // per d block: the slot of chunk v_chunk + 2*db, less the 2*db*CS added at each read.
+  // v_rd1 is the base of the second read (rows +4): with the D = 64 row swizzle the
+  // upper-half lanes find rows 0-3 at positions 4-7 and rows 4-7 at positions 0-3.
+  const bool v_swz = L::V_ROW_SWIZZLE && (vi & 1);
+  int v_rd[DB], v_rd1[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-    v_rd[db] = ((8 * hh) / RPG) * RG + ((8 * hh) % RPG + (vi >> 2)) * 16 +
+  for (int db = 0; db < DB; ++db) {
+    v_rd[db] = ((8 * hh) / RPG) * RG + ((8 * hh) % RPG + (vi >> 2) + (v_swz ? 4 : 0)) * 16 +
                (L::v_slot(v_chunk + 2 * db) - 2 * db) * CS + ((vi >> 1) & 1) * 8;
+    v_rd1[db] = v_rd[db] - (v_swz ? 128 : 0);
+  }
 
   auto acc_key = [&](int kb, int r) { return 32 * kb + key_perm(8 * (r >> 2) + 4 * hh + (r & 3)); };
 
@@ -307,7 +329,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   // One K/V tile: prefetch tile t+1 into `nxt`, compute tile t from `cur`. `next_off`
   // holds the row offsets of tile t+1 (read from the table during the previous step).
-  uint32_t next_off[C::LOADS];
+  uint32_t next_off[2 * C::LOADS];
   auto tile_step = [&](int t, const char* cur, char* nxt) {
     if (t + 1 < Tn) dma_tile(next_off, nxt, t + 1);
     if (t + 2 < Tn) read_offs(t + 2, next_off);
@@ -400,7 +422,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const char* a0 = vs + v_rd[db] + ((32 * kb + 16 * ch) / RPG) * RG + 2 * db * CS;
-          const char* a1 = vs + v_rd[db] + ((32 * kb + 16 * ch + 4) / RPG) * RG + ((32 * kb + 16 * ch + 4) % RPG) * 16 -
+          const char* a1 = vs + v_rd1[db] + ((32 * kb + 16 * ch + 4) / RPG) * RG + ((32 * kb + 16 * ch + 4) % RPG) * 16 -
                            ((32 * kb + 16 * ch) % RPG) * 16 + 2 * db * CS;
           const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)a0);
           const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)a1);
