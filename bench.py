@@ -162,8 +162,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (head sharding is a design note only); "
-              "run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (sharding by head is described, "
+              "not built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -102,3 +102,16 @@ def test_clock_sampler_reads_the_marked_level(tmp_path):
     s.samples = [(0.0, 1900.0), (1.0, 1950.0), (2.0, 1920.0), (3.0, 2400.0)]
     assert s.median(0.5, 2.5) == (1950.0, 2)
     assert s.median(5.0, 6.0) == (None, 0)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus N > 1 (or a multi-rank launch) exits with status 2
+    and says why, before touching torch or the GPU."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for args, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "4"})):
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), *args], capture_output=True, text=True,
+                           env={**os.environ, **env}, timeout=120)
+        assert r.returncode == 2
+        assert "one GPU" in r.stderr and r.stdout == ""
