@@ -85,7 +85,7 @@ def test_committed_traffic_records_are_consistent():
 
 
 def test_clock_sampler_reads_the_marked_level(tmp_path):
-    """bench.py's clock sampler takes the level marked '*' in the driver's pp_dpm_sclk text
+    """bench.py's clock sampler takes the level marked '*' in the amdgpu kernel driver's pp_dpm_sclk text
     (idle: the sleep level; under load: the current frequency between min and max)."""
     import sys
     sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
