@@ -30,6 +30,7 @@
 //     loads and output stores are non-temporal, so that L2 keeps the window's K/V for
 //     the other query tiles.
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "attn_launch.hpp"
@@ -43,15 +44,14 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-// Decode a workgroup into (batch*head, window, query tile), placing consecutive
-// logical tiles on the same XCD.
+// Decode work item `bid` of `total` into (batch*head, window, query tile), placing
+// consecutive logical tiles on the same XCD (item i runs on XCD i % 8: a workgroup's
+// items are blockIdx.x + k * gridDim.x, with gridDim.x a multiple of 8 when it loops).
 struct TileId {
   int32_t bh, win, qtile;
 };
 
-__device__ __forceinline__ TileId decode_tile(const AttnParams& p) {
-  const uint32_t bid = blockIdx.x;
-  const uint32_t total = gridDim.x;
+__device__ __forceinline__ TileId decode_tile(const AttnParams& p, uint32_t bid, uint32_t total) {
   const uint32_t xcd = bid % kNumXcd;
   const uint32_t idx = bid / kNumXcd;
   const uint32_t per = total / kNumXcd;
@@ -160,12 +160,13 @@ __device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t rs, uint32
   __builtin_amdgcn_raw_buffer_store_b128(x, rs, off, 0, kCachePolicyNT);
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void win_attn_bf16_kernel(const uint16_t* __restrict__ q,
-                                                                    const uint16_t* __restrict__ k,
-                                                                    const uint16_t* __restrict__ v,
-                                                                    uint16_t* __restrict__ out,
-                                                                    AttnParams p) {
+// One work item: query tile tile.qtile of window tile.win of head tile.bh. EXT enables the
+// routed window and the pooled memory; without them the key/value stream is the window's
+// own tiles and the kernel needs fewer scalar registers.
+template <int D, int NW, bool EXT>
+__device__ __forceinline__ void win_attn_bf16_item(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                   const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
+                                                   const AttnParams& p, uint32_t item, uint32_t total) {
   using C = Bf16Cfg<D, NW>;
   using L = TileLayout<D>;
   constexpr int BN = C::BN, BM = C::BM, DK = C::DK, DB = C::DB;
@@ -177,7 +178,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char stage1[C::STAGE_BYTES];
 
-  const int tid = threadIdx.x;
+  // threadIdx.x through an opaque move: in the item loop of the persistent kernel the
+  // compiler would otherwise hoist the lane-derived values of the prologue and keep them
+  // live across the tile loop (spills at D = 128).
+  int tid;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"(int(threadIdx.x)));
   const int lane = tid & 63;
   // The wave index is the same on every lane. Saying so keeps the LDS addresses derived from
   // it (the DMA destinations) in scalar registers: 10 fewer VGPRs at D = 128 and no
@@ -186,7 +191,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  const TileId tile = decode_tile(p);
+  const TileId tile = decode_tile(p, item, total);
   const int64_t base = int64_t(tile.bh) * p.head_stride;
   const WinOrigin org = window_origin(p.map, uint32_t(tile.win));
   const uint32_t head_bytes = uint32_t(p.head_stride) * 2u;
@@ -195,12 +200,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // The key/value stream is the window's Tw tiles, then (§3.3) as many tiles of the routed
   // window, if any, then (§3.2) mem_tiles tiles of the pooled memory, a plain [n_mem, D]
   // block per head.
-  int32_t routed = p.route != nullptr ? p.route[int64_t(tile.bh) * p.n_win + tile.win] : -1;
+  int32_t routed = EXT && p.route != nullptr ? p.route[int64_t(tile.bh) * p.n_win + tile.win] : -1;
   if (routed < 0 || routed >= p.n_win) routed = -1;
   const WinOrigin org_r = window_origin(p.map, uint32_t(routed < 0 ? 0 : routed));
   const int Tw = p.kv_tiles;
   const int Tr = routed < 0 ? 0 : Tw;
-  const int Tn = Tw + Tr + p.mem_tiles;
+  const int Tn = EXT ? Tw + Tr + p.mem_tiles : Tw;
   const int64_t mem_base = int64_t(tile.bh) * int64_t(p.n_mem) * D;
   const uint32_t mem_bytes = uint32_t(p.n_mem) * uint32_t(L::ROW_BYTES);
   const __amdgpu_buffer_rsrc_t kmrs = make_rsrc(static_cast<const uint16_t*>(p.kmem) + mem_base, mem_bytes);
@@ -222,7 +227,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   };
   // Byte offset of row r of key/value tile t (window tile, or memory tile past Tw).
   auto tile_row_offset = [&](int t, int r) __attribute__((always_inline)) -> uint32_t {
-    if (t < Tw) return row_offset(t * BN + r);
+    if (!EXT || t < Tw) return row_offset(t * BN + r);
     if (t < Tw + Tr) {
       const int local = (t - Tw) * BN + r;
       return local < p.wtok ? uint32_t(token_of(p.map, org_r, uint32_t(local))) * uint32_t(L::ROW_BYTES)
@@ -233,7 +238,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   };
   // row_off: LOADS byte offsets of the lane's K rows, then LOADS of its V rows
   auto dma_tile = [&](const uint32_t* row_off, char* st, int t) __attribute__((always_inline)) {
-    const bool mem = t >= Tw + Tr;
+    const bool mem = EXT && t >= Tw + Tr;
     const __amdgpu_buffer_rsrc_t ks = mem ? kmrs : krs;
     const __amdgpu_buffer_rsrc_t vs = mem ? vmrs : vrs;
 #pragma unroll
@@ -365,7 +370,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
     // ragged last tile of the window, the routed window or the memory: keys past the end
     // get -inf
-    const int lim = t < Tw ? p.wtok - t * BN : t < Tw + Tr ? p.wtok - (t - Tw) * BN : p.n_mem - (t - Tw - Tr) * BN;
+    const int lim = !EXT || t < Tw ? p.wtok - t * BN : t < Tw + Tr ? p.wtok - (t - Tw) * BN : p.n_mem - (t - Tw - Tr) * BN;
     if (lim < BN) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -481,6 +486,44 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 }
 
+// Argument block of the two kernels below, as the kernel ABI lays it out.
+struct Bf16KernelArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* out;
+  AttnParams p;
+  uint32_t total;
+};
+
+// Plain shifted-window attention: a persistent grid of (at most) one workgroup per CU that
+// walks the work items blockIdx.x, blockIdx.x + gridDim.x, ... This drops the CU's gap
+// between workgroups, which is a visible share of a 16-tile item.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void win_attn_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ out, AttnParams p, uint32_t total) {
+  for (uint32_t item = blockIdx.x; item < total; item += gridDim.x) {
+    // The parameters are read from the argument segment again for each item, through a
+    // pointer the compiler cannot see through; kept in scalar registers across the loop
+    // they would spill.
+    using ArgPtr = const __attribute__((address_space(4))) AttnParams*;
+    ArgPtr pp = (ArgPtr)((const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr() +
+                         offsetof(Bf16KernelArgs, p));
+    asm volatile("" : "+s"(pp));
+    win_attn_bf16_item<D, NW, false>(q, k, v, out, *(const AttnParams*)pp, item, total);
+    __syncthreads();  // the next item's prologue rewrites LDS the epilogue may still read
+  }
+}
+
+// With a routed window (§3.3) and/or pooled memory (§3.2): one work item per workgroup.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void win_attn_bf16_ext_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ out, AttnParams p, uint32_t total) {
+  win_attn_bf16_item<D, NW, true>(q, k, v, out, p, blockIdx.x, total);
+}
+
 // ---------------------------------------------------------------------------------
 // fp32 kernel: one wave per 64 query rows, one query row per lane, K/V tiles of 32 keys
 // in LDS read as broadcasts. Plain fp32 FMA arithmetic throughout (no reduced-precision
@@ -497,7 +540,7 @@ __global__ __launch_bounds__(64) void win_attn_f32_kernel(const float* __restric
   __shared__ __attribute__((aligned(16))) float Ks[BN * D];
   __shared__ __attribute__((aligned(16))) float Vs[BN * D];
   const int lane = threadIdx.x;
-  const TileId tile = decode_tile(p);
+  const TileId tile = decode_tile(p, blockIdx.x, gridDim.x);
   const int64_t base = int64_t(tile.bh) * p.head_stride;
   const WinOrigin org = window_origin(p.map, uint32_t(tile.win));
   const int row = tile.qtile * BM + lane;
@@ -809,6 +852,28 @@ hipError_t launch_pool_kv(const void* k, const void* v, void* kmem, void* vmem, 
 }
 
 // ---------------------------------------------------------------------------------
+// Workgroups of the persistent bf16 kernel: one per CU of the current device (a workgroup
+// takes most of a CU's LDS), rounded down to a multiple of the XCD count so that every
+// workgroup's items stay on its XCD. Queried once per device.
+static hipError_t persistent_slots(uint32_t* slots) {
+  static uint32_t cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && cache[dev] != 0) {
+    *slots = cache[dev];
+    return hipSuccess;
+  }
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  uint32_t n = uint32_t(cus) / kNumXcd * kNumXcd;
+  if (n == 0) n = kNumXcd;
+  if (dev >= 0 && dev < 64) cache[dev] = n;
+  *slots = n;
+  return hipSuccess;
+}
+
 template <int D, int NW>
 static hipError_t launch_bf16(const void* q, const void* k, const void* v, void* out, AttnParams p,
                               hipStream_t stream) {
@@ -818,9 +883,21 @@ static hipError_t launch_bf16(const void* q, const void* k, const void* v, void*
   p.mem_tiles = (p.n_mem + C::BN - 1) / C::BN;
   const uint64_t blocks = uint64_t(p.q_tiles) * uint64_t(p.n_win) * uint64_t(p.heads_total);
   if (blocks == 0 || blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((win_attn_bf16_kernel<D, NW>), dim3(uint32_t(blocks)), dim3(C::NT), 0, stream,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), p);
+  const auto qp = static_cast<const uint16_t*>(q);
+  const auto kp = static_cast<const uint16_t*>(k);
+  const auto vp = static_cast<const uint16_t*>(v);
+  const auto op = static_cast<uint16_t*>(out);
+  if (p.route != nullptr || p.n_mem > 0) {
+    hipLaunchKernelGGL((win_attn_bf16_ext_kernel<D, NW>), dim3(uint32_t(blocks)), dim3(C::NT), 0, stream, qp, kp, vp,
+                       op, p, uint32_t(blocks));
+  } else {
+    uint32_t slots = 0;
+    const hipError_t e = persistent_slots(&slots);
+    if (e != hipSuccess) return e;
+    const uint32_t grid = blocks < slots ? uint32_t(blocks) : slots;
+    hipLaunchKernelGGL((win_attn_bf16_kernel<D, NW>), dim3(grid), dim3(C::NT), 0, stream, qp, kp, vp, op, p,
+                       uint32_t(blocks));
+  }
   return hipGetLastError();
 }
 
