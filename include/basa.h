@@ -17,7 +17,8 @@
  *   - Tensors are contiguous [B, heads, N, head_dim], N = T*H*W tokens flattened
  *     row-major over (t, h, w). q, k, v, out hold the same element type.
  *   - All tensor pointers are DEVICE pointers owned by the caller and must be 16-byte
- *     aligned. The library allocates nothing and keeps no state between calls.
+ *     aligned. The library allocates nothing. Its only state is the compute-unit count of
+ *     each device, read on the first bf16 call there and cached (thread-safe).
  *   - Calls are asynchronous on `stream` (0 = the null stream) and return once the work
  *     is enqueued. Argument errors are reported before any HIP call is made; no entry
  *     point aborts, throws or prints.

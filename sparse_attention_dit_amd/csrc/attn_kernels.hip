@@ -10,7 +10,9 @@
 // window's keys and values are followed by a shared set of pooled memory tokens, and the
 // per-row log-sum-exp is written for merging with other attention results (App. A.1).
 //
-// bf16 kernel layout (one workgroup = one (batch*head, window, query tile)):
+// bf16 kernel layout (one work item = one (batch*head, window, query tile); plain windowed
+// attention runs a persistent grid of one workgroup per CU over the items, the routed/memory
+// variant one workgroup per item):
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q rows kept
 //     in registers). In the 32x32 accumulator lane l holds column l%32 and rows
 //     8*(r/4) + 4*(l/32) + r%4, so every lane owns ONE query row: row max and row sum
@@ -32,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+
+#include <atomic>
 
 #include "attn_launch.hpp"
 #include "index_map.hpp"
@@ -856,20 +860,24 @@ hipError_t launch_pool_kv(const void* k, const void* v, void* kmem, void* vmem, 
 // takes most of a CU's LDS), rounded down to a multiple of the XCD count so that every
 // workgroup's items stay on its XCD. Queried once per device.
 static hipError_t persistent_slots(uint32_t* slots) {
-  static uint32_t cache[64];
+  static std::atomic<uint32_t> cache[64];  // 0 = not read yet; concurrent first reads agree
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < 64 && cache[dev] != 0) {
-    *slots = cache[dev];
-    return hipSuccess;
+  const bool cached = dev >= 0 && dev < 64;
+  if (cached) {
+    const uint32_t n = cache[dev].load(std::memory_order_relaxed);
+    if (n != 0) {
+      *slots = n;
+      return hipSuccess;
+    }
   }
   int cus = 0;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   uint32_t n = uint32_t(cus) / kNumXcd * kNumXcd;
   if (n == 0) n = kNumXcd;
-  if (dev >= 0 && dev < 64) cache[dev] = n;
+  if (cached) cache[dev].store(n, std::memory_order_relaxed);
   *slots = n;
   return hipSuccess;
 }
