@@ -10,9 +10,8 @@
 // window's keys and values are followed by a shared set of pooled memory tokens, and the
 // per-row log-sum-exp is written for merging with other attention results (App. A.1).
 //
-// bf16 kernel layout (one work item = one (batch*head, window, query tile); plain windowed
-// attention runs a persistent grid of one workgroup per CU over the items, the routed/memory
-// variant one workgroup per item):
+// bf16 kernel layout (one work item = one (batch*head, window, query tile); a persistent
+// grid of one workgroup per CU walks the items):
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q rows kept
 //     in registers). In the 32x32 accumulator lane l holds column l%32 and rows
 //     8*(r/4) + 4*(l/32) + r%4, so every lane owns ONE query row: row max and row sum
@@ -500,13 +499,13 @@ struct Bf16KernelArgs {
   uint32_t total;
 };
 
-// Plain shifted-window attention: a persistent grid of (at most) one workgroup per CU that
-// walks the work items blockIdx.x, blockIdx.x + gridDim.x, ... This drops the CU's gap
-// between workgroups, which is a visible share of a 16-tile item.
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void win_attn_bf16_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ out, AttnParams p, uint32_t total) {
+// Both kernels run a persistent grid of (at most) one workgroup per CU that walks the work
+// items blockIdx.x, blockIdx.x + gridDim.x, ... This drops the CU's gap between
+// workgroups, which is a visible share of a 16-tile item.
+template <int D, int NW, bool EXT>
+__device__ __forceinline__ void win_attn_bf16_items(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                    const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
+                                                    uint32_t total) {
   for (uint32_t item = blockIdx.x; item < total; item += gridDim.x) {
     // The parameters are read from the argument segment again for each item, through a
     // pointer the compiler cannot see through; kept in scalar registers across the loop
@@ -515,17 +514,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     ArgPtr pp = (ArgPtr)((const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr() +
                          offsetof(Bf16KernelArgs, p));
     asm volatile("" : "+s"(pp));
-    win_attn_bf16_item<D, NW, false>(q, k, v, out, *(const AttnParams*)pp, item, total);
+    win_attn_bf16_item<D, NW, EXT>(q, k, v, out, *(const AttnParams*)pp, item, total);
     __syncthreads();  // the next item's prologue rewrites LDS the epilogue may still read
   }
 }
 
-// With a routed window (§3.3) and/or pooled memory (§3.2): one work item per workgroup.
+// Plain shifted-window attention (§3.1).
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void win_attn_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ out, AttnParams p, uint32_t total) {
+  (void)p;  // read through the argument segment
+  win_attn_bf16_items<D, NW, false>(q, k, v, out, total);
+}
+
+// With a routed window (§3.3) and/or pooled memory (§3.2).
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void win_attn_bf16_ext_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ out, AttnParams p, uint32_t total) {
-  win_attn_bf16_item<D, NW, true>(q, k, v, out, p, blockIdx.x, total);
+  (void)p;
+  win_attn_bf16_items<D, NW, true>(q, k, v, out, total);
 }
 
 // ---------------------------------------------------------------------------------
@@ -895,17 +904,16 @@ static hipError_t launch_bf16(const void* q, const void* k, const void* v, void*
   const auto kp = static_cast<const uint16_t*>(k);
   const auto vp = static_cast<const uint16_t*>(v);
   const auto op = static_cast<uint16_t*>(out);
-  if (p.route != nullptr || p.n_mem > 0) {
-    hipLaunchKernelGGL((win_attn_bf16_ext_kernel<D, NW>), dim3(uint32_t(blocks)), dim3(C::NT), 0, stream, qp, kp, vp,
-                       op, p, uint32_t(blocks));
-  } else {
-    uint32_t slots = 0;
-    const hipError_t e = persistent_slots(&slots);
-    if (e != hipSuccess) return e;
-    const uint32_t grid = blocks < slots ? uint32_t(blocks) : slots;
+  uint32_t slots = 0;
+  const hipError_t e = persistent_slots(&slots);
+  if (e != hipSuccess) return e;
+  const uint32_t grid = blocks < slots ? uint32_t(blocks) : slots;
+  if (p.route != nullptr || p.n_mem > 0)
+    hipLaunchKernelGGL((win_attn_bf16_ext_kernel<D, NW>), dim3(grid), dim3(C::NT), 0, stream, qp, kp, vp, op, p,
+                       uint32_t(blocks));
+  else
     hipLaunchKernelGGL((win_attn_bf16_kernel<D, NW>), dim3(grid), dim3(C::NT), 0, stream, qp, kp, vp, op, p,
                        uint32_t(blocks));
-  }
   return hipGetLastError();
 }
 
