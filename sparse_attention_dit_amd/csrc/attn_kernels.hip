@@ -31,7 +31,6 @@
 //     loads and output stores are non-temporal, so that L2 keeps the window's K/V for
 //     the other query tiles.
 #include <hip/hip_runtime.h>
-#include <stddef.h>
 #include <stdint.h>
 
 #include <atomic>
@@ -489,32 +488,30 @@ __device__ __forceinline__ void win_attn_bf16_item(const uint16_t* __restrict__ 
   }
 }
 
-// Argument block of the two kernels below, as the kernel ABI lays it out.
+// The single argument of the two kernels below: the kernel's argument segment is this
+// struct, so the item loop can re-read the parameters from it by address.
 struct Bf16KernelArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
   uint16_t* out;
   AttnParams p;
-  uint32_t total;
+  uint32_t total;  // work items
 };
 
 // Both kernels run a persistent grid of (at most) one workgroup per CU that walks the work
 // items blockIdx.x, blockIdx.x + gridDim.x, ... This drops the CU's gap between
 // workgroups, which is a visible share of a 16-tile item.
 template <int D, int NW, bool EXT>
-__device__ __forceinline__ void win_attn_bf16_items(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                    const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
-                                                    uint32_t total) {
-  for (uint32_t item = blockIdx.x; item < total; item += gridDim.x) {
+__device__ __forceinline__ void win_attn_bf16_items(const Bf16KernelArgs& a) {
+  for (uint32_t item = blockIdx.x; item < a.total; item += gridDim.x) {
     // The parameters are read from the argument segment again for each item, through a
     // pointer the compiler cannot see through; kept in scalar registers across the loop
     // they would spill.
-    using ArgPtr = const __attribute__((address_space(4))) AttnParams*;
-    ArgPtr pp = (ArgPtr)((const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr() +
-                         offsetof(Bf16KernelArgs, p));
-    asm volatile("" : "+s"(pp));
-    win_attn_bf16_item<D, NW, EXT>(q, k, v, out, *(const AttnParams*)pp, item, total);
+    using ArgPtr = const __attribute__((address_space(4))) Bf16KernelArgs*;
+    ArgPtr ap = (ArgPtr)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(ap));
+    win_attn_bf16_item<D, NW, EXT>(a.q, a.k, a.v, a.out, ((const Bf16KernelArgs*)ap)->p, item, a.total);
     __syncthreads();  // the next item's prologue rewrites LDS the epilogue may still read
   }
 }
@@ -522,19 +519,15 @@ __device__ __forceinline__ void win_attn_bf16_items(const uint16_t* __restrict__
 // Plain shifted-window attention (§3.1).
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void win_attn_bf16_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ out, AttnParams p, uint32_t total) {
-  (void)p;  // read through the argument segment
-  win_attn_bf16_items<D, NW, false>(q, k, v, out, total);
+    Bf16KernelArgs a) {
+  win_attn_bf16_items<D, NW, false>(a);
 }
 
 // With a routed window (§3.3) and/or pooled memory (§3.2).
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void win_attn_bf16_ext_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ out, AttnParams p, uint32_t total) {
-  (void)p;
-  win_attn_bf16_items<D, NW, true>(q, k, v, out, total);
+    Bf16KernelArgs a) {
+  win_attn_bf16_items<D, NW, true>(a);
 }
 
 // ---------------------------------------------------------------------------------
@@ -900,20 +893,21 @@ static hipError_t launch_bf16(const void* q, const void* k, const void* v, void*
   p.mem_tiles = (p.n_mem + C::BN - 1) / C::BN;
   const uint64_t blocks = uint64_t(p.q_tiles) * uint64_t(p.n_win) * uint64_t(p.heads_total);
   if (blocks == 0 || blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
-  const auto qp = static_cast<const uint16_t*>(q);
-  const auto kp = static_cast<const uint16_t*>(k);
-  const auto vp = static_cast<const uint16_t*>(v);
-  const auto op = static_cast<uint16_t*>(out);
+  Bf16KernelArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.out = static_cast<uint16_t*>(out);
+  a.p = p;
+  a.total = uint32_t(blocks);
   uint32_t slots = 0;
   const hipError_t e = persistent_slots(&slots);
   if (e != hipSuccess) return e;
   const uint32_t grid = blocks < slots ? uint32_t(blocks) : slots;
   if (p.route != nullptr || p.n_mem > 0)
-    hipLaunchKernelGGL((win_attn_bf16_ext_kernel<D, NW>), dim3(grid), dim3(C::NT), 0, stream, qp, kp, vp, op, p,
-                       uint32_t(blocks));
+    hipLaunchKernelGGL((win_attn_bf16_ext_kernel<D, NW>), dim3(grid), dim3(C::NT), 0, stream, a);
   else
-    hipLaunchKernelGGL((win_attn_bf16_kernel<D, NW>), dim3(grid), dim3(C::NT), 0, stream, qp, kp, vp, op, p,
-                       uint32_t(blocks));
+    hipLaunchKernelGGL((win_attn_bf16_kernel<D, NW>), dim3(grid), dim3(C::NT), 0, stream, a);
   return hipGetLastError();
 }
 
