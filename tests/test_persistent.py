@@ -6,7 +6,9 @@ than an MI355X has CUs (256), so each workgroup there runs one item; these cases
 several hundred items, so that most workgroups run two to four, in uneven numbers. Every
 output element (and the log-sum-exp where written) is compared with the fp64 reference:
 plain windows (both head dims, a ragged window), pooled memory, and a routed window with
-memory. Bars as everywhere: bf16 rel-L2 <= 5e-3 and max-abs <= 2e-2, LSE max-abs <= 3e-3.
+memory. A second set has item counts just below, at and just above the CU count and twice
+it (255, 256, 257, 513). Bars as everywhere: bf16 rel-L2 <= 5e-3 and max-abs <= 2e-2, LSE
+max-abs <= 3e-3.
 """
 import math
 
@@ -35,6 +37,35 @@ CASES = [
 def work_items(B, heads, grid, window):
     n_win = int(np.prod([g // w for g, w in zip(grid, window)]))
     return B * heads * n_win * math.ceil(int(np.prod(window)) / BM)
+
+
+# item counts just below, at and just above one and two per CU (plain windows, one query
+# tile per window): name, heads, head_dim, grid, window, shift, seed
+EDGE = [
+    ("255-items", 51, 128, (1, 8, 40), (1, 8, 8), (0, 2, 3), 311),
+    ("256-items", 64, 64, (1, 16, 16), (1, 8, 8), (0, 4, 1), 312),
+    ("257-items", 257, 64, (1, 8, 8), (1, 8, 8), (0, 1, 1), 313),
+    ("513-items", 19, 128, (3, 24, 24), (1, 8, 8), (1, 3, 5), 314),
+]
+
+
+def test_edge_item_counts():
+    assert [work_items(1, c[1], c[3], c[4]) for c in EDGE] == [255, 256, 257, 513]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_item_counts_around_the_grid(case):
+    name, heads, d, grid, window, shift, seed = case
+    N = int(np.prod(grid))
+    t = inputs.draw_qkv((1, heads, N, d), "bf16", seed)
+    dev = to_device(t)
+    out = torch.empty_like(dev["q"])
+    log_case(name, "grid", grid, "window", window, "shift", shift)
+    _lib.window_attn_fwd(dev["q"], dev["k"], dev["v"], out, grid, window, shift)
+    torch.cuda.synchronize()
+    ref = O.window_attention(t.f64("q"), t.f64("k"), t.f64("v"), grid, window, shift)
+    assert_parity(to_host(out), ref, "bf16", name)
 
 
 def test_cases_span_several_items_per_workgroup():
