@@ -26,10 +26,11 @@
 //   * Online softmax in fp32 with exp2 and the 1/sqrt(d)*log2(e) scale folded into one
 //     FMA; the running max is only raised (and O rescaled) when a row's max grows by
 //     more than 2^8, which keeps the final O/l exact while skipping most rescales.
-//   * Workgroups are renumbered so that all query tiles of one (head, window) land on
-//     the same XCD (hardware dispatches workgroup i to XCD i % 8) and share its L2. Q
-//     loads and output stores are non-temporal, so that L2 keeps the window's K/V for
-//     the other query tiles.
+//   * Work items are renumbered so that all query tiles of one (head, window) land on
+//     the same XCD (hardware dispatches workgroup i to XCD i % 8; the persistent grid is a
+//     multiple of 8, so a workgroup's items stay on its XCD) and share its L2. Q loads and
+//     output stores are non-temporal, so that L2 keeps the window's K/V for the other
+//     query tiles.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

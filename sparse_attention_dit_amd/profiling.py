@@ -151,7 +151,7 @@ def _kernel_stats(directory: str, dense: int, cmd: str, out: str, bench_json: st
                   "|---|---|---|---|"]
         with open(stats_csv[0]) as f:
             for r in csv.DictReader(f):
-                lines.append(f"| `{r['Name'][:60]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                lines.append(f"| `{r['Name'][:100]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                              f"{float(r['Percentage']):.2f} |")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
