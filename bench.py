@@ -26,8 +26,8 @@ from sparse_attention_dit_amd.configs import BY_NAME  # noqa: E402
 from sparse_attention_dit_amd.profiling import traffic_json_name  # noqa: E402
 
 # MI355X published peaks: dense bf16 MFMA 2.5 PFLOP/s (256 CU x 2.4 GHz x 4096 flop/clk),
-# fp32 vector 157.3 TFLOP/s (256 CU x 2.4 GHz x 256 flop/clk; the fp32 kernel is plain
-# VALU FMA work, so its bound is "alu"), HBM3E 8 TB/s.
+# dense fp32 MFMA 157.3 TFLOP/s (256 CU x 2.4 GHz x 256 flop/clk; the fp32 kernel's products
+# run on v_mfma_f32_32x32x2_f32), HBM3E 8 TB/s.
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
@@ -341,7 +341,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
                    "grid": list(w.grid), "window": list(w.window), "shifts": [list(s) for s in w.shifts],
                    "tokens": w.tokens, "window_tokens": w.window_tokens, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(tflops, 2), "peak": peak,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                      "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": measured_traffic(w.name)},
         "speedup": {"full_attn_ms": round(ms_full, 4), "window_attn_ms": round(ms_per_launch, 4),

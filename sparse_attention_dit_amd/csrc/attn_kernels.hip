@@ -532,38 +532,52 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 }
 
 // ---------------------------------------------------------------------------------
-// fp32 kernel: one wave per 64 query rows, one query row per lane, K/V tiles of 32 keys
-// in LDS read as broadcasts. Plain fp32 FMA arithmetic throughout (no reduced-precision
-// operands), online softmax with exp2. Used for fp32 inputs, where exactness to ~1e-6
-// matters more than speed.
+// fp32 kernel: the bf16 kernel's dataflow on fp32 operands, with v_mfma_f32_32x32x2_f32
+// (fp32 products, fp32 accumulation; no reduced-precision step anywhere).
+//   * A workgroup of 4 waves takes 128 query rows of one (head, window); each wave owns 32
+//     rows and keeps its rows' q in registers as the B operand of S^T = K Q^T. For MFMA step
+//     s, lane half hh supplies d = hh*D/2 + s (the order of the d terms is free), so each
+//     lane's K and Q reads are contiguous.
+//   * S^T accumulator register r of lane (l32, hh) holds key 8*(r/4) + 4*hh + r%4 of query
+//     row l32. After the softmax, register s is exactly the B operand P^T[key][query] of
+//     step s of O^T = V^T P^T, with the A operand V[key][d] read from LDS for the same key.
+//   * K/V tiles of 32 keys pass global -> registers -> LDS, double buffered: the loads of
+//     tile t+1 are in flight while tile t is computed. Row strides are padded (K by 4
+//     floats, V by 8) so that the 16-byte K reads of 32 rows and the 4-byte V reads of
+//     two rows four apart are free of bank conflicts.
+//   * Online softmax in fp32 with exp2, the same lazy max raise as the bf16 kernel.
 template <int D>
-__global__ __launch_bounds__(64) void win_attn_f32_kernel(const float* __restrict__ q,
-                                                          const float* __restrict__ k,
-                                                          const float* __restrict__ v,
-                                                          float* __restrict__ out, AttnParams p) {
-  constexpr int BN = 32;
-  constexpr int BM = 64;
-  constexpr int CH = 8;  // keys per softmax chunk
-  __shared__ __attribute__((aligned(16))) float Ks[BN * D];
-  __shared__ __attribute__((aligned(16))) float Vs[BN * D];
-  const int lane = threadIdx.x;
+struct F32Cfg {
+  static constexpr int NW = 4;
+  static constexpr int NT = NW * 64;
+  static constexpr int BM = NW * 32;         // query rows per workgroup
+  static constexpr int BN = 32;              // keys per K/V tile
+  static constexpr int KS = D + 4;           // K row stride (floats)
+  static constexpr int VS = D + 8;           // V row stride (floats)
+  static constexpr int CPR = D / 4;          // 16-byte chunks per row
+  static constexpr int CH = BN * CPR / NT;   // chunks per thread per tensor per tile
+  static_assert(CH >= 1 && CH * NT == BN * CPR, "tile/thread mismatch");
+};
+
+template <int D>
+__global__ __launch_bounds__(F32Cfg<D>::NT) __attribute__((amdgpu_waves_per_eu(2))) void win_attn_f32_kernel(const float* __restrict__ q,
+                                                                     const float* __restrict__ k,
+                                                                     const float* __restrict__ v,
+                                                                     float* __restrict__ out, AttnParams p) {
+  using C = F32Cfg<D>;
+  constexpr int BN = C::BN, KS = C::KS, VS = C::VS, CPR = C::CPR, CH = C::CH, DB = D / 32;
+  __shared__ __attribute__((aligned(16))) float Ks[2][BN * KS];
+  __shared__ __attribute__((aligned(16))) float Vs[2][BN * VS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
   const TileId tile = decode_tile(p, blockIdx.x, gridDim.x);
   const int64_t base = int64_t(tile.bh) * p.head_stride;
   const WinOrigin org = window_origin(p.map, uint32_t(tile.win));
-  const int row = tile.qtile * BM + lane;
-  const bool valid = row < p.wtok;
-  const int my_tok = valid ? token_of(p.map, org, uint32_t(row)) : 0;
-
-  float qv[D];
-  float o[D];
-#pragma unroll
-  for (int d = 0; d < D; ++d) {
-    qv[d] = valid ? q[base + int64_t(my_tok) * D + d] : 0.0f;
-    o[d] = 0.0f;
-  }
-  float m = -__builtin_inff(), l = 0.0f;
-  const float c = p.scale_log2;
-
   // key/value tiles: the window's, the routed window's if any (§3.3), then those of the
   // pooled memory (§3.2)
   int32_t routed = p.route != nullptr ? p.route[int64_t(tile.bh) * p.n_win + tile.win] : -1;
@@ -574,77 +588,160 @@ __global__ __launch_bounds__(64) void win_attn_f32_kernel(const float* __restric
   const int Tn = Tw + Tr + (p.n_mem + BN - 1) / BN;
   const float* kmem = static_cast<const float*>(p.kmem) + int64_t(tile.bh) * int64_t(p.n_mem) * D;
   const float* vmem = static_cast<const float*>(p.vmem) + int64_t(tile.bh) * int64_t(p.n_mem) * D;
-  for (int t = 0; t < Tn; ++t) {
+  auto tile_rows = [&](int t) -> int {  // valid rows of key/value tile t
+    if (t < Tw) return p.wtok - t * BN;
+    if (t < Tw + Tr) return p.wtok - (t - Tw) * BN;
+    return p.n_mem - (t - Tw - Tr) * BN;
+  };
+
+  // q row of this lane (B operand of S^T): d = hh*D/2 .. hh*D/2 + D/2 - 1
+  const int qlocal = tile.qtile * C::BM + wave * 32 + l32;
+  const bool qvalid = qlocal < p.wtok;
+  const int qtok = qvalid ? token_of(p.map, org, uint32_t(qlocal)) : 0;
+  float qf[D / 2];
+  {
+    const float4* src = reinterpret_cast<const float4*>(q + base + int64_t(qtok) * D + hh * (D / 2));
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) {
+      const float4 x = qvalid ? src[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      qf[4 * i + 0] = x.x;
+      qf[4 * i + 1] = x.y;
+      qf[4 * i + 2] = x.z;
+      qf[4 * i + 3] = x.w;
+    }
+  }
+
+  // Tile loads: thread tid moves chunks e = tid + j*NT (row e / CPR, chunk e % CPR) of K and V.
+  float4 kreg[CH], vreg[CH];
+  auto load_tile = [&](int t) __attribute__((always_inline)) {
+    const int nrows = tile_rows(t);
     const bool mem = t >= Tw + Tr;
     const bool rt = !mem && t >= Tw;
-    const int nrows = mem ? p.n_mem - (t - Tw - Tr) * BN : p.wtok - (rt ? t - Tw : t) * BN;
-    __syncthreads();
-    // 64 lanes load 32 rows: two lanes per row, each half of the row
-    {
-      const int r = lane >> 1;
-      const int half = lane & 1;
-      float* kd = &Ks[r * D + half * (D / 2)];
-      float* vd = &Vs[r * D + half * (D / 2)];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int e = tid + j * C::NT;
+      const int r = e / CPR;
+      const int cc = e % CPR;
+      kreg[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      vreg[j] = kreg[j];
       if (r < nrows) {
         const float* ks;
         const float* vs;
         if (mem) {
-          const int64_t j = int64_t((t - Tw - Tr) * BN + r) * D + half * (D / 2);
-          ks = kmem + j;
-          vs = vmem + j;
+          const int64_t off = int64_t((t - Tw - Tr) * BN + r) * D + cc * 4;
+          ks = kmem + off;
+          vs = vmem + off;
         } else {
           const int tok = rt ? token_of(p.map, org_r, uint32_t((t - Tw) * BN + r))
                              : token_of(p.map, org, uint32_t(t * BN + r));
-          ks = k + base + int64_t(tok) * D + half * (D / 2);
-          vs = v + base + int64_t(tok) * D + half * (D / 2);
+          const int64_t off = base + int64_t(tok) * D + cc * 4;
+          ks = k + off;
+          vs = v + off;
         }
-#pragma unroll
-        for (int d = 0; d < D / 2; ++d) {
-          kd[d] = ks[d];
-          vd[d] = vs[d];
-        }
-      } else {
-#pragma unroll
-        for (int d = 0; d < D / 2; ++d) {
-          kd[d] = 0.0f;
-          vd[d] = 0.0f;
-        }
+        kreg[j] = *reinterpret_cast<const float4*>(ks);
+        vreg[j] = *reinterpret_cast<const float4*>(vs);
       }
     }
+  };
+  auto store_tile = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int e = tid + j * C::NT;
+      const int r = e / CPR;
+      const int cc = e % CPR;
+      *reinterpret_cast<float4*>(&Ks[b][r * KS + cc * 4]) = kreg[j];
+      *reinterpret_cast<float4*>(&Vs[b][r * VS + cc * 4]) = vreg[j];
+    }
+  };
+
+  f32x16_t oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+  float m_run = -__builtin_inff(), l_run = 0.0f;
+  const float c = p.scale_log2;
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int t = 0; t < Tn; ++t) {
+    const int cur = t & 1;
+    if (t + 1 < Tn) load_tile(t + 1);  // in flight during this tile's products
+
+    // S^T = K Q^T: 32 keys x 32 query rows, D/2 steps of two d each
+    f32x16_t sacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
+    const float* kr = &Ks[cur][l32 * KS + hh * (D / 2)];
+#pragma unroll
+    for (int s = 0; s < D / 2; s += 4) {
+      const float4 kk = *reinterpret_cast<const float4*>(kr + s);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kk.x, qf[s + 0], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kk.y, qf[s + 1], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kk.z, qf[s + 2], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kk.w, qf[s + 3], sacc, 0, 0, 0);
+    }
+    // keys past the end of a ragged tile get -inf
+    const int nrows = tile_rows(t);
+    if (nrows < BN) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + 4 * hh + (r & 3) >= nrows) sacc[r] = -__builtin_inff();
+    }
+
+    // online softmax (the row's two lane halves agree on the running max)
+    float mx = sacc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+    mx = wave_half_max(mx) * c;
+    const bool need = mx > m_run + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float m_new = need ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    const float neg_m = -m_run;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sacc[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, neg_m));
+      lsum += sacc[r];
+    }
+    l_run += lsum;
+
+    // O^T += V^T P^T: step s pairs key 8*(s/4) + 4*hh + s%4 of V with register s of P^T
+    const float* vr = &Vs[cur][(4 * hh) * VS + l32];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const int key_off = (8 * (s >> 2) + (s & 3)) * VS;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[key_off + 32 * db], sacc[s], oacc[db], 0, 0, 0);
+    }
+
+    if (t + 1 < Tn) store_tile(cur ^ 1);  // everyone finished reading that buffer last step
     __syncthreads();
-    const int nk = min(BN, nrows);
-    for (int j0 = 0; j0 < nk; j0 += CH) {
-      float s[CH];
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int d = 0; d < D; ++d) acc = __builtin_fmaf(qv[d], Ks[(j0 + j) * D + d], acc);
-        s[j] = (j0 + j < nk) ? acc * c : -__builtin_inff();
-        mx = fmaxf(mx, s[j]);
-      }
-      const float m_new = fmaxf(m, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-      l *= alpha;
-#pragma unroll
-      for (int d = 0; d < D; ++d) o[d] *= alpha;
-#pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        const float pj = __builtin_amdgcn_exp2f(s[j] - m_new);
-        l += pj;
-#pragma unroll
-        for (int d = 0; d < D; ++d) o[d] = __builtin_fmaf(pj, Vs[(j0 + j) * D + d], o[d]);
-      }
-      m = m_new;
-    }
   }
-  if (valid) {
+
+  const float l = wave_half_sum(l_run);
+  if (qvalid) {
     const float inv = 1.0f / l;
+    float* orow = out + base + int64_t(qtok) * D;
 #pragma unroll
-    for (int d = 0; d < D; ++d) out[base + int64_t(my_tok) * D + d] = o[d] * inv;
-    if (p.lse != nullptr)
-      p.lse[int64_t(tile.bh) * p.n_tokens + my_tok] = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)  // registers 4g..4g+3: d = 32db + 8g + 4hh + 0..3
+        *reinterpret_cast<float4*>(orow + 32 * db + 8 * g + 4 * hh) =
+            make_float4(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv,
+                        oacc[db][4 * g + 3] * inv);
+    if (p.lse != nullptr && hh == 0)
+      p.lse[int64_t(tile.bh) * p.n_tokens + qtok] = (m_run + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
   }
 }
 
@@ -915,12 +1012,13 @@ static hipError_t launch_bf16(const void* q, const void* k, const void* v, void*
 template <int D>
 static hipError_t launch_f32(const void* q, const void* k, const void* v, void* out, AttnParams p,
                              hipStream_t stream) {
-  p.q_tiles = (p.wtok + 63) / 64;
-  p.kv_tiles = (p.wtok + 31) / 32;
-  p.mem_tiles = (p.n_mem + 31) / 32;
+  using C = F32Cfg<D>;
+  p.q_tiles = (p.wtok + C::BM - 1) / C::BM;
+  p.kv_tiles = (p.wtok + C::BN - 1) / C::BN;
+  p.mem_tiles = (p.n_mem + C::BN - 1) / C::BN;
   const uint64_t blocks = uint64_t(p.q_tiles) * uint64_t(p.n_win) * uint64_t(p.heads_total);
   if (blocks == 0 || blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((win_attn_f32_kernel<D>), dim3(uint32_t(blocks)), dim3(64), 0, stream,
+  hipLaunchKernelGGL((win_attn_f32_kernel<D>), dim3(uint32_t(blocks)), dim3(C::NT), 0, stream,
                      static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
                      static_cast<float*>(out), p);
   return hipGetLastError();
