@@ -72,6 +72,26 @@ def test_peaky_logits():
     assert_parity(got, ref, "bf16", "peaky logits")
 
 
+# fp32 at sizes that fill the chip (every element): the FLUX-1024 shape in fp32 (8 K/V tiles
+# of 32 keys per window, 768 workgroups) and a 3-D ragged window at d = 64.
+F32_AT_SIZE = [
+    ("f32-flux1024-shape", 24, 128, (1, 64, 64), (1, 16, 16), (0, 8, 8), 401),
+    ("f32-3d-ragged-d64", 16, 64, (6, 20, 30), (3, 10, 15), (2, 5, -4), 402),
+]
+
+
+@pytest.mark.parametrize("case", F32_AT_SIZE, ids=[c[0] for c in F32_AT_SIZE])
+def test_f32_at_size_every_element(case):
+    name, heads, d, grid, window, shift, seed = case
+    N = int(np.prod(grid))
+    t = inputs.draw_qkv((1, heads, N, d), "f32", seed)
+    dev = to_device(t)
+    log_case(name, "seed", seed, "shape", (1, heads, N, d), "shift", shift)
+    got = to_host(run_window(dev, grid, window, shift))
+    ref = O.window_attention(t.f64("q"), t.f64("k"), t.f64("v"), grid, window, shift)
+    assert_parity(got, ref, "f32", name)
+
+
 def _sample_rows(N, seed, grid, window, shift, count=96):
     rng = np.random.default_rng(1000 + seed)
     rows = set(rng.choice(N, size=count, replace=False).tolist())
