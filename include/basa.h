@@ -20,7 +20,9 @@
  *     aligned. The library allocates nothing. Its only state is the compute-unit count of
  *     each device, read on the first bf16 call there and cached (thread-safe).
  *   - Calls are asynchronous on `stream` (0 = the null stream) and return once the work
- *     is enqueued. Argument errors are reported before any HIP call is made; no entry
+ *     is enqueued. They allocate, clear and synchronise nothing, so a sequence of calls can
+ *     be captured in a HIP graph and replayed (after a first call on the device, outside
+ *     the capture, has read its compute-unit count). Argument errors are reported before any HIP call is made; no entry
  *     point aborts, throws or prints.
  *   - The softmax scale is 1/sqrt(head_dim); softmax statistics are kept in fp32.
  *   - Supported: dtype BASA_DTYPE_F32 or BASA_DTYPE_BF16, head_dim 64 or 128.

@@ -1,0 +1,98 @@
+"""The entry points inside a captured HIP graph.
+
+A DiT's denoising loop calls the attention once per layer and step with the same shapes,
+which is what graph capture is for. The library's calls make no allocation, no memset
+and no synchronisation, so they can be captured. Each test captures a sequence of calls
+into a graph (`torch.cuda.graph`), then replays it several times with new inputs copied
+into the captured tensors, with eager work and a synchronisation between replays, and
+checks that every replay equals the eager result bit for bit (the kernels use no atomics,
+so a launch is deterministic).
+"""
+import pytest
+import torch
+
+from gpu_util import log_case
+from sparse_attention_dit_amd import _lib
+
+pytestmark = pytest.mark.gpu
+
+GRID, WINDOW, SHIFTS = (2, 32, 48), (1, 16, 16), [(0, 0, 0), (1, 8, 8)]
+REPLAYS = 3
+
+
+def _new_inputs(shape, dtype, seed):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return [torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(dtype) for _ in range(3)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_window_attention_graph_replays(dtype):
+    N = GRID[0] * GRID[1] * GRID[2]
+    shape = (1, 4, N, 128)
+    q, k, v = _new_inputs(shape, dtype, 1)
+    outs = [torch.empty_like(q) for _ in SHIFTS]
+    log_case("graph window attention", dtype, shape, GRID, WINDOW, SHIFTS)
+
+    # warm the library (first call reads the device's CU count) outside the capture
+    for s, o in zip(SHIFTS, outs):
+        _lib.window_attn_fwd(q, k, v, o, GRID, WINDOW, s)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for s, o in zip(SHIFTS, outs):
+            _lib.window_attn_fwd(q, k, v, o, GRID, WINDOW, s)
+
+    for r in range(REPLAYS):
+        nq, nk, nv = _new_inputs(shape, dtype, 100 + r)
+        q.copy_(nq)
+        k.copy_(nk)
+        v.copy_(nv)
+        graph.replay()
+        torch.cuda.synchronize()
+        for s, o in zip(SHIFTS, outs):
+            ref = torch.empty_like(q)
+            _lib.window_attn_fwd(nq, nk, nv, ref, GRID, WINDOW, s)  # eager, on fresh tensors
+            torch.cuda.synchronize()
+            assert torch.equal(o, ref), f"replay {r}, shift {s}: graph output differs from eager"
+
+
+def test_memory_path_graph_replays():
+    """Pooling and attention with memory (and its log-sum-exp) captured together."""
+    T, H, W = GRID
+    pool = (4, 4)
+    N = T * H * W
+    n_mem = T * (H // pool[0]) * (W // pool[1])
+    shape = (1, 4, N, 128)
+    q, k, v = _new_inputs(shape, torch.bfloat16, 2)
+    kmem = torch.empty((1, 4, n_mem, 128), dtype=torch.bfloat16, device="cuda")
+    vmem = torch.empty_like(kmem)
+    out = torch.empty_like(q)
+    lse = torch.empty((1, 4, N), dtype=torch.float32, device="cuda")
+    log_case("graph memory path", shape, GRID, WINDOW, pool)
+
+    def chain(q_, k_, v_, km_, vm_, o_, l_):
+        _lib.pool_kv(k_, v_, km_, vm_, GRID, pool)
+        _lib.window_attn_mem_fwd(q_, k_, v_, km_, vm_, o_, GRID, WINDOW, SHIFTS[1], lse=l_)
+
+    chain(q, k, v, kmem, vmem, out, lse)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        chain(q, k, v, kmem, vmem, out, lse)
+
+    for r in range(REPLAYS):
+        nq, nk, nv = _new_inputs(shape, torch.bfloat16, 200 + r)
+        q.copy_(nq)
+        k.copy_(nk)
+        v.copy_(nv)
+        graph.replay()
+        torch.cuda.synchronize()
+        rkm, rvm = torch.empty_like(kmem), torch.empty_like(vmem)
+        rout, rlse = torch.empty_like(out), torch.empty_like(lse)
+        chain(nq, nk, nv, rkm, rvm, rout, rlse)
+        torch.cuda.synchronize()
+        assert torch.equal(kmem, rkm) and torch.equal(vmem, rvm), f"replay {r}: pooled memory differs"
+        assert torch.equal(out, rout), f"replay {r}: output differs from eager"
+        assert torch.equal(lse, rlse), f"replay {r}: log-sum-exp differs from eager"
