@@ -1,4 +1,4 @@
-"""GPU parity on seeded random configurations, through the C ABI, against the fp64 reference.
+"""GPU parity on 40 seeded random configurations, through the C ABI, against the fp64 reference.
 
 Each case draws the grid, window, shift, dtype, head_dim, batch and heads together, and
 one of three paths:
@@ -28,7 +28,7 @@ from oracle import routing_oracle as R
 from sparse_attention_dit_amd import _lib, inputs
 
 LSE_TOL = {"bf16": 3e-3, "f32": 1e-5}
-N_CASES = 24
+N_CASES = 40
 
 
 def _draw_case(i):
