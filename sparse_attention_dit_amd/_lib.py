@@ -98,6 +98,8 @@ def _check_tensors(q, k, v, out):
             raise BasaError(2, f"{name} must be [B, heads, N, head_dim]")
         if t.shape != q.shape or t.dtype != q.dtype:
             raise BasaError(2, f"{name} shape/dtype {tuple(t.shape)}/{t.dtype} differs from q")
+        if t.device != q.device:
+            raise BasaError(2, f"{name} is on {t.device}, q on {q.device}")
 
 
 def window_attn_fwd(q, k, v, out, grid, window, shift, stream=None) -> None:

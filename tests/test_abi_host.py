@@ -172,3 +172,14 @@ def test_index_map_header_matches_oracle_table(index_tool, tmp_path, grid, windo
     got = np.fromfile(out, dtype=np.int32)
     ref = O.window_members(grid, window, shift).ravel()
     assert np.array_equal(got, ref)
+
+
+def test_binding_rejects_host_tensors_before_any_library_call():
+    """The Python binding checks its tensors before it calls an entry point: host tensors
+    are refused with BASA_ERR_NULL's code."""
+    import torch
+    from sparse_attention_dit_amd import _lib
+    q = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16)
+    with pytest.raises(_lib.BasaError) as e:
+        _lib.window_attn_fwd(q, q, q, torch.empty_like(q), (1, 8, 8), (1, 8, 8), (0, 0, 0))
+    assert e.value.status == 1 and "device tensor" in str(e.value)
