@@ -10,8 +10,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-# BASA_LIB may name another build of the same library (e.g. a tuning variant)
-LIB_PATH = os.environ.get("BASA_LIB") or os.path.join(_PKG, "libbasa.so")
+# Always the in-tree build: no environment variable or search path can substitute another
+# library for the one the tests, the smoke check and the benchmark report on.
+LIB_PATH = os.path.join(_PKG, "libbasa.so")
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
@@ -64,6 +65,17 @@ def load() -> ctypes.CDLL:
     lib.basa_version.restype = i
     _lib = lib
     return lib
+
+
+def library_info() -> dict:
+    """Which library is loaded: its path relative to the repository root and the first 16
+    hex digits of the SHA-256 of its bytes (printed by the smoke check, recorded by the
+    benchmark)."""
+    import hashlib
+    load()
+    with open(LIB_PATH, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()[:16]
+    return {"path": os.path.relpath(LIB_PATH, os.path.dirname(_PKG)), "sha256_16": digest}
 
 
 def status_string(status: int) -> str:

@@ -79,6 +79,13 @@ int run_attention(const void* q, const void* k, const void* v, const int32_t* ro
     if (n_mem > 0 && (overlaps2(lse, lse_bytes, kmem, mem_bytes) || overlaps2(lse, lse_bytes, vmem, mem_bytes)))
       return BASA_ERR_ALIAS;
   }
+  // route is an input the kernel reads at the start of every work item while other
+  // workgroups already write out and lse
+  if (route) {
+    const int64_t route_bytes = bh * (N / (int64_t(wt) * wh * ww)) * 4;
+    if (overlaps2(out, bytes, route, route_bytes)) return BASA_ERR_ALIAS;
+    if (lse && overlaps2(lse, bh * N * 4, route, route_bytes)) return BASA_ERR_ALIAS;
+  }
 
   basa::AttnParams p;
   p.map = basa::make_winmap(T, H, W, wt, wh, ww, reduce_mod(st, T), reduce_mod(sh, H), reduce_mod(sw, W));

@@ -142,6 +142,10 @@ def test_routing_argument_errors():
     assert routed(rt=G + 2) == 7
     assert routed(n_mem=4) == 1
     assert routed(lse=D) == 4
+    # the route table is an input: it must not overlap out or lse
+    assert routed(rt=D) == 4
+    assert routed(rt=D + 128 * 256 * 2 * 2 - 4) == 4      # last int32 of out
+    assert routed(rt=G, lse=G - 4 * 2 * 256 + 4) == 4      # lse's last row over route's first
 
 
 @pytest.fixture(scope="module")
@@ -183,3 +187,17 @@ def test_binding_rejects_host_tensors_before_any_library_call():
     with pytest.raises(_lib.BasaError) as e:
         _lib.window_attn_fwd(q, q, q, torch.empty_like(q), (1, 8, 8), (1, 8, 8), (0, 0, 0))
     assert e.value.status == 1 and "device tensor" in str(e.value)
+
+
+def test_binding_loads_only_the_in_tree_library():
+    """The binding always loads the library built in the package directory: an environment
+    variable naming another build is not consulted (checked in a fresh interpreter)."""
+    import sys
+    assert _lib.LIB_PATH == os.path.join(ROOT, "sparse_attention_dit_amd", "libbasa.so")
+    info = _lib.library_info()
+    assert info["path"] == os.path.join("sparse_attention_dit_amd", "libbasa.so")
+    assert len(info["sha256_16"]) == 16
+    env = dict(os.environ, BASA_LIB="/nonexistent/libother.so")
+    res = subprocess.run([sys.executable, "-c", "from sparse_attention_dit_amd import _lib; print(_lib.LIB_PATH)"],
+                         cwd=ROOT, env=env, capture_output=True, text=True, check=True)
+    assert res.stdout.strip() == _lib.LIB_PATH

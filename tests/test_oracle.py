@@ -170,6 +170,29 @@ def test_softmax_rows_sum_to_one():
         np.testing.assert_allclose(P.sum(axis=1), 1.0, rtol=0, atol=P.shape[1] * 2.0 ** -52)
 
 
+def test_window_weights_equal_masked_dense_attention_map():
+    """Each window's weight matrix is the block of the dense softmax map, built with the
+    block-diagonal mask of the shifted frame (numpy.roll of an index grid), that the
+    window's members index; the map is zero between tokens of different windows. Scaled
+    q makes the rows far from uniform, so a wrong scale or a transposed product fails."""
+    grid, window, s = (2, 8, 8), (2, 4, 4), (1, 2, 3)
+    N = 128
+    q, k, _ = _rand_qkv((1, 1, N, 16), seed=17)
+    q = q * 3.0
+    win = _shifted_window_ids(grid, window, s)
+    mask = win[:, None] == win[None, :]
+    S = (q[0, 0] @ k[0, 0].T) / math.sqrt(16)
+    S = np.where(mask, S, -np.inf)
+    P = np.exp(S - S.max(axis=1, keepdims=True))
+    P = P / P.sum(axis=1, keepdims=True)
+    assert (P[~mask] == 0).all()
+    table = O.window_members(grid, window, s)
+    mats = O.window_weights(q, k, grid, window, s)
+    assert len(mats) == len(table)
+    for members, Pw in zip(table, mats):
+        np.testing.assert_allclose(Pw, P[np.ix_(members, members)], rtol=0, atol=1e-14)
+
+
 def test_closed_forms():
     grid, window, s = (2, 6, 8), (1, 3, 4), (1, 2, 3)
     N = 96
