@@ -31,7 +31,7 @@ from sparse_attention_dit_amd.profiling import traffic_json_name  # noqa: E402
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
-DEFAULT_WORKLOAD = "flux-2048-128x128-w32"
+DEFAULT_WORKLOAD = "flux-4096-256x256-w32"
 
 
 class ClockSampler:
@@ -94,6 +94,41 @@ def measured_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def host_info():
+    """CPU model, logical CPUs available to this process, physical cores, NumPy version and
+    the BLAS library NumPy calls (with its thread count)."""
+    import numpy as np
+    model, phys = None, set()
+    try:
+        with open("/proc/cpuinfo") as f:
+            cur = {}
+            for line in f:
+                if ":" in line:
+                    key, val = (x.strip() for x in line.split(":", 1))
+                    cur[key] = val
+                    if key == "model name" and model is None:
+                        model = val
+                elif cur:
+                    phys.add((cur.get("physical id"), cur.get("core id")))
+                    cur = {}
+            if cur:
+                phys.add((cur.get("physical id"), cur.get("core id")))
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = {"library": libs[0].get("internal_api"), "version": libs[0].get("version"),
+                    "threads": libs[0].get("num_threads")}
+    except Exception:  # pragma: no cover - informational only
+        pass
+    return {"cpu_model": model, "logical_cpus_available": len(os.sched_getaffinity(0)),
+            "physical_cores": len(phys) if phys and None not in next(iter(phys)) else None,
+            "numpy": np.__version__, "blas": blas}
+
+
 def cpu_baseline(w, min_s: float, pool: int = 0, route: bool = False):
     """Time the fp64 oracle (as it stands) on a bounded sample of the workload: whole
     (shift, head) slices of the windowed attention (with pooled memory when pool > 0; the
@@ -139,6 +174,7 @@ def cpu_baseline(w, min_s: float, pool: int = 0, route: bool = False):
         "unit": "TFLOP/s",
         "cores": threads if threads is not None else len(os.sched_getaffinity(0)),
         "kind": "oracle",
+        "host": host_info(),
         "sample": f"{slices} (shift, head) slices of {w.num_windows} windows each (one step = "
                   f"{len(w.shifts) * w.heads}), fp64 numpy, one head's q/k/v drawn with the workload seed "
                   f"({flops / 1e9:.1f} GFLOP in {elapsed:.1f} s)",
@@ -253,19 +289,42 @@ def main():
     launches = args.steps * len(w.shifts)
     ms_per_launch = ms_total / launches
 
-    # each shift of the cycle on its own (same launches, timed per shift)
-    per_shift_ms = []
-    for s in w.shifts:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
-            if args.pool or args.route:
-                attend(w.shifts.index(s), s)
-            else:
-                _lib.window_attn_fwd(dev["q"], dev["k"], dev["v"], out, w.grid, w.window, s, stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        per_shift_ms.append(round(e0.elapsed_time(e1) / args.steps, 4))
+    # Sustained rate: the same steps again, one event pair around every launch (or, with
+    # --pool/--route, every shift's group of launches), for at least 20 steps and 200 ms of
+    # GPU time; reported as the median launch time overall and per shift, with the clock
+    # held over that span.
+    def launch(i, s):
+        if args.pool or args.route:
+            attend(i, s)
+        else:
+            _lib.window_attn_fwd(dev["q"], dev["k"], dev["v"], out, w.grid, w.window, s, stream)
+
+    sus_steps = max(20, int(200.0 / max(ms_per_step, 1e-3)) + 1)
+    sus_clock = ClockSampler().start()
+    pairs = []
+    torch.cuda.synchronize()
+    t_sus0 = time.perf_counter()
+    for _ in range(sus_steps):
+        for i, s in enumerate(w.shifts):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch(i, s)
+            e1.record(stream)
+            pairs.append((i, e0, e1))
+    torch.cuda.synchronize()
+    t_sus1 = time.perf_counter()
+    sus_clock.stop()
+    per_launch = [(i, e0.elapsed_time(e1)) for i, e0, e1 in pairs]
+    span_ms = pairs[0][1].elapsed_time(pairs[-1][2])
+
+    def median(xs):
+        xs = sorted(xs)
+        n = len(xs)
+        return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+    sus_med = median([ms for _, ms in per_launch])
+    per_shift_ms = [round(median([ms for j, ms in per_launch if j == i]), 4) for i in range(len(w.shifts))]
+    sus_sclk, sus_samples = sus_clock.median(t_sus0, t_sus1)
     pool_ms = None
     if args.pool:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -349,6 +408,13 @@ def main():
                     "ratio": round(measured / theoretical, 4),
                     "full_attn_tflops": round(w.full_flops() / (ms_full * 1e-3) / 1e12, 2)},
         "per_shift_ms": per_shift_ms,
+        "sustained": {
+            "steps": sus_steps, "launches": len(per_launch), "span_ms": round(span_ms, 2),
+            "median_ms_per_launch": round(sus_med, 4), "mean_ms_per_launch": round(span_ms / len(per_launch), 4),
+            "tflops_median": round(flops_launch / (sus_med * 1e-3) / 1e12, 2),
+            "frac_median": round(flops_launch / (sus_med * 1e-3) / 1e12 / peak, 4),
+            "vs_value": round((flops_launch / (sus_med * 1e-3) / 1e12) / tflops, 4),
+            "sclk_mhz_median": sus_sclk, "sclk_samples": sus_samples},
         "io_gbs": round(io_gbs, 1),
         # The core clock under this load: the chip is power-limited, so it runs below the
         # 2.4 GHz the peak assumes; frac_at_clock is achieved / (peak * sclk / 2400).
@@ -356,6 +422,7 @@ def main():
             "median": sclk_mhz, "samples": sclk_samples, "source": "pp_dpm_sclk",
             "frac_at_clock": round(tflops / (peak * sclk_mhz / 2400.0), 4)},
         "kernel_hash": kernel_hash(),
+        "library": _lib.library_info(),
     }
     if args.pool:
         G_bytes = 2 * w.batch * w.heads * n_mem * w.head_dim * (2 if w.dtype == "bf16" else 4)

@@ -133,18 +133,45 @@ def _kernel_stats(directory: str, dense: int, cmd: str, out: str, bench_json: st
         lines.append(f"| {label} | {s['calls']} | {s['avg_us']:.2f} | {s['median_us']:.2f} | {s['min_us']:.2f} | "
                      f"{s['max_us']:.2f} |")
     if bench_json:
+        from sparse_attention_dit_amd.configs import BY_NAME
         with open(bench_json) as f:
             b = json.loads(f.read().strip().splitlines()[-1])
-        # bench.py's windowed launches, in order: clock settle, warm-up, the timed steps, ...
+        w = BY_NAME[b["config"]["workload"]]
+        # bench.py's windowed launches, in order: clock settle, warm-up, the timed steps,
+        # the sustained steps, ...
         per_step = len(b["config"]["shifts"])
         first = (b["clock_settle_steps"] + b["warmup"]) * per_step
         timed = _stats_table(dur[first:first + b["steps"] * per_step])
         lines.append(f"| windowed, bench.py's timed steps only | {timed['calls']} | {timed['avg_us']:.2f} | "
                      f"{timed['median_us']:.2f} | {timed['min_us']:.2f} | {timed['max_us']:.2f} |")
+        sus = None
+        if "sustained" in b:
+            s0 = first + b["steps"] * per_step
+            sus = _stats_table(dur[s0:s0 + b["sustained"]["launches"]])
+            lines.append(f"| windowed, bench.py's sustained steps | {sus['calls']} | {sus['avg_us']:.2f} | "
+                         f"{sus['median_us']:.2f} | {sus['min_us']:.2f} | {sus['max_us']:.2f} |")
+        peak = 2516.6 if w.dtype == "bf16" else 157.3
+        flops = w.window_flops()
+        sclk = (b.get("sclk_mhz") or {}).get("median")
+        frac = flops / (timed["avg_us"] * 1e-6) / 1e12 / peak
         lines += ["", "bench.py's own line for the same run (HIP events around the timed steps):", "",
                   f"- windowed: {b['speedup']['window_attn_ms'] * 1e3:.2f} µs per launch "
-                  f"({b['value']} TFLOP/s); rocprofv3 average over the same launches: {timed['avg_us']:.2f} µs",
+                  f"({b['value']} TFLOP/s, frac {b['roofline']['frac']}); rocprofv3 average over the same "
+                  f"launches: {timed['avg_us']:.2f} µs, i.e. {flops / 1e9:.2f} GFLOP / {timed['avg_us']:.2f} µs = "
+                  f"{flops / (timed['avg_us'] * 1e-6) / 1e12:.1f} TFLOP/s = {frac:.4f} of {peak} TFLOP/s",
+                  f"- kernel time per step from the trace: {timed['avg_us'] * per_step / 1e3:.4f} ms; bench.py's "
+                  f"ms_per_step: {b['ms_per_step']}",
                   f"- dense: {b['speedup']['full_attn_ms'] * 1e3:.2f} µs per launch"]
+        if sclk:
+            lines.append(f"- core clock held over the timed steps (pp_dpm_sclk median): {sclk:.0f} MHz; fraction of "
+                         f"the peak at that clock (peak x sclk / 2400): {frac * 2400.0 / sclk:.4f}")
+        if sus is not None:
+            sb = b["sustained"]
+            lines.append(f"- sustained: bench.py median {sb['median_ms_per_launch'] * 1e3:.2f} µs per launch over "
+                         f"{sb['launches']} launches ({sb['span_ms']:.0f} ms, clock {sb['sclk_mhz_median']} MHz); "
+                         f"rocprofv3 median over the same launches {sus['median_us']:.2f} µs")
+        lines.append(f"- library: `{b.get('library', {}).get('path')}` sha256 {b.get('library', {}).get('sha256_16')}, "
+                     f"kernel source digest `{b.get('kernel_hash')}`")
     stats_csv = glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True)
     if stats_csv:
         lines += ["", "rocprofv3 --stats (all kernels of the run):", "", "| kernel | calls | avg µs | share % |",
@@ -213,6 +240,84 @@ def _traffic(a) -> None:
           f"({(fetch_b + write_b) / algo:.3f} x algorithmic)")
 
 
+# Counter passes of the MFMA/LDS record. Each pass stays within one collection's hardware
+# limits (at most 8 SQ and 2 GRBM counters); MfmaUtil and LDSBankConflict are rocprofv3's
+# derived metrics over SQ_VALU_MFMA_BUSY_CYCLES / SQ_LDS_BANK_CONFLICT and GRBM_GUI_ACTIVE.
+COUNTER_PASSES = {
+    "mfma": ("MfmaUtil", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+             "SQ_INSTS_MFMA", "SQ_VALU_MFMA_COEXEC_CYCLES"),
+    "valu": ("LDSBankConflict", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_VALU",
+             "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS"),
+}
+SIMDS = 1024  # 256 CUs x 4 SIMDs
+MFMA_FLOP = {"bf16": 32 * 32 * 16 * 2, "f32": 32 * 32 * 2 * 2}  # v_mfma_f32_32x32x16_bf16 / 32x32x2_f32
+
+
+def _counters(a) -> None:
+    from sparse_attention_dit_amd.build import kernel_hash
+    from sparse_attention_dit_amd.configs import BY_NAME
+
+    w = BY_NAME[a.workload]
+    vals = {}
+    for directory, names in ((a.mfma, COUNTER_PASSES["mfma"]), (a.valu, COUNTER_PASSES["valu"])):
+        for n in names:
+            vals[n], count = _counter_per_dispatch(directory, n, a.kernel)
+            vals[n + "#dispatches"] = count
+    flops = w.window_flops() if a.what == "window" else w.full_flops()
+    mfma_alg = flops / MFMA_FLOP[w.dtype]
+    mops_flop = vals["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+    rec = {
+        "workload": w.name, "launch": a.what, "kernel": a.kernel, "kernel_hash": kernel_hash(),
+        "raw_per_dispatch": {k: v for k, v in vals.items() if not k.endswith("#dispatches")},
+        "dispatches": {k[:-11]: v for k, v in vals.items() if k.endswith("#dispatches")},
+        "algorithmic_flop_per_launch": flops,
+        "mfma_flop_counted_over_algorithmic": round(mops_flop / flops, 4) if w.dtype == "bf16" else None,
+        "mfma_instructions_over_algorithmic": round(vals["SQ_INSTS_MFMA"] / mfma_alg, 4),
+        "mfma_util_pct": round(vals["MfmaUtil"], 2),
+        "coexec_cycles_per_simd": round(vals["SQ_VALU_MFMA_COEXEC_CYCLES"] / SIMDS),
+        "lds_bank_conflict_pct_of_time": round(vals["LDSBankConflict"], 2),
+        "lds_bank_conflict_over_lds_active": round(vals["SQ_LDS_BANK_CONFLICT"] / vals["SQ_LDS_IDX_ACTIVE"], 4),
+        # MfmaUtil divides the summed busy cycles by the largest GUI-active count of one
+        # instance; the raw GRBM_GUI_ACTIVE row is the sum over instances
+        "gui_active_cycles_one_instance": round(vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (vals["MfmaUtil"] / 100.0) / SIMDS),
+        "mfma_busy_cycles_per_simd": round(vals["SQ_VALU_MFMA_BUSY_CYCLES"] / SIMDS),
+        "valu_per_mfma": round(vals["SQ_INSTS_VALU"] / vals["SQ_INSTS_MFMA"], 3),
+        "trans_f32_per_mfma": round(vals["SQ_INSTS_VALU_TRANS_F32"] / vals["SQ_INSTS_MFMA"], 3),
+        "lds_instr_per_mfma": round(vals["SQ_INSTS_LDS"] / vals["SQ_INSTS_MFMA"], 3),
+        "commands": a.cmd,
+    }
+    os.makedirs(a.out_dir, exist_ok=True)
+    stem = f"{a.kernel}.{w.name}.{a.what}.counters"
+    with open(os.path.join(a.out_dir, stem + ".json"), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    md = [f"# MFMA, VALU and LDS counters of {a.kernel}, workload {w.name} ({a.what} launch)", "",
+          "Commands (from the repository root; one rocprofv3 counter pass each):", "", "```", *a.cmd, "```", "",
+          "| quantity | value |", "|---|---|",
+          f"| algorithmic FLOP per launch | {flops / 1e9:.2f} GFLOP |",
+          f"| MFMA FLOP counted (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) / algorithmic | "
+          f"{rec['mfma_flop_counted_over_algorithmic']} |",
+          f"| MFMA instructions (SQ_INSTS_MFMA) / algorithmic count | {rec['mfma_instructions_over_algorithmic']} |",
+          f"| MFMA utilisation (MfmaUtil: busy cycles / (GUI-active cycles x SIMDs)) | {rec['mfma_util_pct']} % |",
+          f"| MFMA-busy cycles per SIMD / GUI-active cycles of one instance | {rec['mfma_busy_cycles_per_simd']} / "
+          f"{rec['gui_active_cycles_one_instance']} |",
+          f"| MFMA-busy cycles with a VALU instruction co-issued, per SIMD | {rec['coexec_cycles_per_simd']} |",
+          f"| LDS stalled by bank conflicts (LDSBankConflict, % of time per CU) | "
+          f"{rec['lds_bank_conflict_pct_of_time']} % |",
+          f"| SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE | {rec['lds_bank_conflict_over_lds_active']} |",
+          f"| VALU instructions per MFMA | {rec['valu_per_mfma']} |",
+          f"| fp32 transcendental instructions per MFMA | {rec['trans_f32_per_mfma']} |",
+          f"| LDS instructions per MFMA | {rec['lds_instr_per_mfma']} |",
+          "", "Raw values per dispatch (mean over the profiled dispatches):", "",
+          "| counter | value |", "|---|---|"]
+    md += [f"| {k} | {v:.6g} |" for k, v in rec["raw_per_dispatch"].items()]
+    md += ["", f"Kernel source digest: `{rec['kernel_hash']}`"]
+    with open(os.path.join(a.out_dir, stem + ".md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    print(f"wrote {stem}: MfmaUtil {rec['mfma_util_pct']} %, MFMA/alg {rec['mfma_instructions_over_algorithmic']}, "
+          f"LDS conflict {rec['lds_bank_conflict_over_lds_active']}")
+
+
 def main(argv=None) -> None:
     ap = argparse.ArgumentParser(prog="python -m sparse_attention_dit_amd.profiling")
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -233,7 +338,18 @@ def main(argv=None) -> None:
     t.add_argument("--workload", required=True)
     t.add_argument("--cmd", action="append", required=True)
     t.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
+    c = sub.add_parser("counters")
+    c.add_argument("--mfma", required=True, help="output directory of the 'mfma' counter pass")
+    c.add_argument("--valu", required=True, help="output directory of the 'valu' counter pass")
+    c.add_argument("--workload", required=True)
+    c.add_argument("--what", choices=("window", "full"), default="window")
+    c.add_argument("--kernel", default=ATTN_KERNEL, help="substring naming the profiled kernel")
+    c.add_argument("--cmd", action="append", required=True)
+    c.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
     a = ap.parse_args(argv)
+    if a.cmd_name == "counters":
+        _counters(a)
+        return
     if a.cmd_name == "run":
         _run(a.what, a.workload, a.iters)
     elif a.cmd_name == "kernel-stats":

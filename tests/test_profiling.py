@@ -115,3 +115,41 @@ def test_bench_refuses_more_than_one_gpu():
                            env={**os.environ, **env}, timeout=120)
         assert r.returncode == 2
         assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_counter_summary(tmp_path):
+    """MFMA/VALU/LDS record: counters are averaged over the kernel's dispatches and related
+    to the algorithmic MFMA count of the workload."""
+    k = "void basa::win_attn_bf16_kernel<128, 8>(...)"
+    wl = BY_NAME["flux-2048-128x128-w32"]
+    n_mfma = wl.window_flops() / (32 * 32 * 16 * 2)
+    mfma = [(k, "MfmaUtil", 50.0), (k, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 1000.0), (k, "GRBM_GUI_ACTIVE", 16000.0),
+            (k, "SQ_INSTS_VALU_MFMA_MOPS_BF16", wl.window_flops() / 512), (k, "SQ_INSTS_MFMA", n_mfma),
+            (k, "SQ_VALU_MFMA_COEXEC_CYCLES", 1024 * 300.0), ("other", "SQ_INSTS_MFMA", 1.0)]
+    valu = [(k, "LDSBankConflict", 3.0), (k, "SQ_LDS_BANK_CONFLICT", 250.0), (k, "SQ_LDS_IDX_ACTIVE", 1000.0),
+            (k, "SQ_INSTS_VALU", 4 * n_mfma), (k, "SQ_INSTS_VALU_TRANS_F32", n_mfma), (k, "SQ_INSTS_LDS", n_mfma / 2)]
+    _counters(tmp_path / "m", mfma)
+    _counters(tmp_path / "v", valu)
+    out = tmp_path / "out"
+    profiling.main(["counters", "--mfma", str(tmp_path / "m"), "--valu", str(tmp_path / "v"), "--workload", wl.name,
+                    "--cmd", "c1", "--cmd", "c2", "--out-dir", str(out)])
+    rec = json.load(open(out / f"win_attn_bf16_kernel.{wl.name}.window.counters.json"))
+    assert rec["mfma_flop_counted_over_algorithmic"] == 1.0
+    assert rec["mfma_instructions_over_algorithmic"] == 1.0
+    assert rec["mfma_util_pct"] == 50.0
+    assert rec["mfma_busy_cycles_per_simd"] == 1000
+    assert rec["gui_active_cycles_one_instance"] == 2000
+    assert rec["lds_bank_conflict_over_lds_active"] == 0.25
+    assert rec["valu_per_mfma"] == 4.0 and rec["trans_f32_per_mfma"] == 1.0 and rec["lds_instr_per_mfma"] == 0.5
+    assert rec["kernel_hash"] == kernel_hash()
+    assert (out / f"win_attn_bf16_kernel.{wl.name}.window.counters.md").exists()
+
+
+def test_host_info_fields():
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    info = bench.host_info()
+    assert info["logical_cpus_available"] >= 1
+    assert info["numpy"]
+    assert set(info) == {"cpu_model", "logical_cpus_available", "physical_cores", "numpy", "blas"}
