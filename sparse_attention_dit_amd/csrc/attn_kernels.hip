@@ -87,7 +87,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 // Row of the 32-key block that feeds accumulator row m: bits 2 and 3 swapped.
-__device__ __forceinline__ int key_perm(int m) {
+__host__ __device__ constexpr int key_perm(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
@@ -163,6 +163,219 @@ __device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t rs, uint32
   __builtin_amdgcn_raw_buffer_store_b128(x, rs, off, 0, kCachePolicyNT);
 }
 
+// Workgroup barrier that waits only for each wave's own LDS accesses (s_waitcnt lgkmcnt(0),
+// gfx9 immediate 0xC07F), not for its outstanding global loads and stores as __syncthreads()
+// does. The empty asm statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Per-lane view of the bf16 tile math: the lane's LDS read bases and the three products of a
+// K/V step. A wave owns 32 query rows; lane (l32, hh) holds query row l32 of the wave and
+// half hh of its head_dim.
+template <int D, int NW>
+struct Bf16Lane {
+  using C = Bf16Cfg<D, NW>;
+  using L = TileLayout<D>;
+  static constexpr int BN = C::BN, DK = C::DK, DB = C::DB;
+  static constexpr int RPG = L::RPG, CS = L::CS, RG = L::RG, CPR = L::CPR;
+  static constexpr int QG = 32 / RPG;  // row groups of one wave's 32 query rows
+
+  int l32, hh;
+  int ld_slot, ld_row, v_ld_row;  // chunk slot and group row the lane moves in a wave-wide load
+  uint32_t k_chunk_off, v_chunk_off;
+  int q_rd, k_rd;
+  int v_rd[DB], v_rd1[DB];
+
+  __device__ __forceinline__ Bf16Lane(int lane, int wave) {
+    l32 = lane & 31;
+    hh = lane >> 5;
+    // K/V/Q tile loads: lane j moves 16 bytes, chunk slot j / RPG of row (group*RPG + j % RPG)
+    ld_slot = lane / RPG;
+    ld_row = lane % RPG;
+    k_chunk_off = uint32_t(ld_slot) * 16u;
+    v_chunk_off = uint32_t(L::v_slot(ld_slot)) * 16u;
+    // row of its group that the lane loads for V (differs from ld_row only for the upper-half
+    // chunks of D = 64; see TileLayout)
+    v_ld_row = (L::V_ROW_SWIZZLE && ld_slot >= CPR / 2) ? (ld_row ^ 4) : ld_row;
+    // B operand of S^T: lane holds d = hh*D/2 + 8*kk .. +7 of query row wave*32 + l32
+    const int qrow = wave * 32 + l32;
+    q_rd = (qrow / RPG) * RG + (qrow % RPG) * 16 + hh * (CPR / 2) * CS;
+    // K (A operand of S^T): row 32*kb + key_perm(l32), chunk hh*CPR/2 + kk
+    const int krow = key_perm(l32);
+    k_rd = (krow / RPG) * RG + (krow % RPG) * 16 + hh * (CPR / 2) * CS;
+    // V^T (A operand of O^T) by transpose reads: in each 16-lane group lane i supplies the
+    // address of 4 consecutive d of key row (i / 4) and receives one d of 4 keys. Lane
+    // (g, i, hh) of block db reads d-chunk 2*db + g (lower half of d) for i%4 in {0, 2} and
+    // CPR/2 + 2*db + g (upper half) for i%4 in {1, 3}; i%4 in {2, 3} take the chunk's upper
+    // 8 bytes. Per d block: the slot of chunk v_chunk + 2*db, less the 2*db*CS added at each
+    // read. v_rd1 is the base of the second read (rows +4): with the D = 64 row swizzle the
+    // upper-half lanes find rows 0-3 at positions 4-7 and rows 4-7 at positions 0-3.
+    const int vg = l32 >> 4;
+    const int vi = lane & 15;
+    const int v_chunk = ((vi & 1) ? CPR / 2 : 0) + vg;
+    const bool v_swz = L::V_ROW_SWIZZLE && (vi & 1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      v_rd[db] = ((8 * hh) / RPG) * RG + ((8 * hh) % RPG + (vi >> 2) + (v_swz ? 4 : 0)) * 16 +
+                 (L::v_slot(v_chunk + 2 * db) - 2 * db) * CS + ((vi >> 1) & 1) * 8;
+      v_rd1[db] = v_rd[db] - (v_swz ? 128 : 0);
+    }
+  }
+
+  // Key of accumulator register r of block kb: 32kb + key_perm(8(r/4) + 4hh + r%4), which is
+  // 8hh plus a compile-time constant (key_perm moves hh to bit 3).
+  static constexpr int acc_key0(int kb, int r) { return 32 * kb + key_perm(8 * (r >> 2) + (r & 3)); }
+
+  __device__ __forceinline__ void load_q(const char* qbuf, bf16x8_t* qf) const {
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qbuf + q_rd + kk * CS);
+  }
+
+  // S^T = K Q^T for one 64-key tile (two 32-key blocks) from the K tile at `ks`.
+  __device__ __forceinline__ void s_products(const char* ks, const bf16x8_t* qf, f32x16_t* sacc) const {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+    bf16x8_t kf[DK][2];
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        kf[kk][kb] = *reinterpret_cast<const bf16x8_t*>(ks + k_rd + kb * (32 / RPG) * RG + kk * CS);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk][kb], qf[kk], sacc[kb], 0, 0, 0);
+  }
+
+  // Online softmax (fp32, exp2 with the scale c = log2(e)/sqrt(d) folded into one FMA) of one
+  // tile's scores; P^T packed to bf16 as the B operand of O^T += V^T P^T. Keys at index >= lim
+  // within the tile (the ragged end of a key range) get -inf. The running max is raised, and O
+  // and l rescaled, only when a row's max grows by more than 2^8.
+  __device__ __forceinline__ void softmax(int lim, float c, f32x16_t* sacc, bf16x8_t* pf, float& m_run, float& l_run,
+                                          f32x16_t* oacc) const {
+    if (lim < BN) {
+      const int lim_l = lim - 8 * hh;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (acc_key0(kb, r) >= lim_l) sacc[kb][r] = -__builtin_inff();
+    }
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = wave_half_max(mx) * c;
+    const bool need = mx > m_run + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float m_new = need ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    const float neg_m = -m_run;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+        u32x4_t packed;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * ch + 2 * e], c, neg_m));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * ch + 2 * e + 1], c, neg_m));
+          // The row sum adds the bf16-rounded p that the PV product uses. The packed word
+          // goes through a scalar temporary: bit-casting the vector element directly
+          // (packed[e]) makes hipcc 7.2 feed the same register to every v_dot2c.
+          const uint32_t w = pack_bf16x2(p0, p1);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                                __builtin_bit_cast(bf16x2_t, 0x3f803f80u), lsum, false);
+          packed[e] = w;
+        }
+        pf[kb * 2 + ch] = __builtin_bit_cast(bf16x8_t, packed);
+      }
+    }
+    l_run += lsum;
+  }
+
+  // O^T += V^T P^T for one tile from the V tile at `vs`; the 16 keys of chunk (kb, ch) are
+  // rows 32kb + 16ch + 8hh + 0..7
+  __device__ __forceinline__ void pv_products(const char* vs, const bf16x8_t* pf, f32x16_t* oacc) const {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const char* a0 = vs + v_rd[db] + ((32 * kb + 16 * ch) / RPG) * RG + 2 * db * CS;
+          const char* a1 = vs + v_rd1[db] + ((32 * kb + 16 * ch + 4) / RPG) * RG + ((32 * kb + 16 * ch + 4) % RPG) * 16 -
+                           ((32 * kb + 16 * ch) % RPG) * 16 + 2 * db * CS;
+          const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)a0);
+          const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)a1);
+          const bf16x8_t vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb * 2 + ch], oacc[db], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // Normalise the wave's 32 output rows by 1/l and store each at its original (un-shifted)
+  // position. The packed rows go through the wave's part of `buf` (QG / PASSES row groups,
+  // laid out like a K tile) in PASSES rounds of 32 / PASSES rows, so that each wave-wide store
+  // writes RPG whole rows (16 lanes per 256-byte row) instead of 16 bytes of 64 different
+  // rows. row_off[r] is the byte offset (in the resource `ors`) of the tile's query row r;
+  // rows past the window hold an offset beyond the resource range and are dropped.
+  template <int PASSES>
+  __device__ __forceinline__ void store_rows(char* buf, const f32x16_t* oacc, float inv, const uint32_t* row_off,
+                                             __amdgpu_buffer_rsrc_t ors, int wave) const {
+    constexpr int RP = 32 / PASSES;  // rows per pass
+    constexpr int GP = QG / PASSES;  // row groups per pass
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+      const int lr = l32 - pass * RP;
+      if (PASSES == 1 || (lr >= 0 && lr < RP)) {
+        const int base = (wave * GP + lr / RPG) * RG + (lr % RPG) * 16 + hh * (CPR / 2) * CS;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            u32x4_t w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              w[e] = pack_bf16x2(oacc[db][8 * half + 2 * e] * inv, oacc[db][8 * half + 2 * e + 1] * inv);
+            // chunk hh*CPR/2 + 2*db + half of the row
+            *reinterpret_cast<u32x4_t*>(buf + base + (2 * db + half) * CS) = w;
+          }
+      }
+      // Lanes read what other lanes of the wave just wrote. The hardware keeps one wave's LDS
+      // accesses in order; this compiler barrier stops the compiler from treating the reads as
+      // private to each lane (it would otherwise reuse the previous pass's values in the lanes
+      // that did not write in this pass).
+      asm volatile("" ::: "memory");
+      u32x4_t w[GP];
+#pragma unroll
+      for (int i = 0; i < GP; ++i)
+        w[i] = *reinterpret_cast<const u32x4_t*>(buf + (wave * GP + i) * RG + ld_slot * CS + ld_row * 16);
+#pragma unroll
+      for (int i = 0; i < GP; ++i)
+        buffer_store16(ors, row_off[wave * 32 + pass * RP + i * RPG + ld_row] + k_chunk_off, w[i]);
+    }
+  }
+};
+
 // One work item: query tile tile.qtile of window tile.win of head tile.bh. EXT enables the
 // routed window and the pooled memory; without them the key/value stream is the window's
 // own tiles and the kernel needs fewer scalar registers.
@@ -172,8 +385,10 @@ __device__ __forceinline__ void win_attn_bf16_item(const uint16_t* __restrict__ 
                                                    const AttnParams& p, uint32_t item, uint32_t total) {
   using C = Bf16Cfg<D, NW>;
   using L = TileLayout<D>;
+  using LN = Bf16Lane<D, NW>;
   constexpr int BN = C::BN, BM = C::BM, DK = C::DK, DB = C::DB;
-  constexpr int RPG = L::RPG, CS = L::CS, RG = L::RG, CPR = L::CPR;
+  constexpr int RPG = L::RPG, RG = L::RG;
+  constexpr int QG = LN::QG;
 
   // Two stages as separate objects: with the stage fixed at compile time in each half of
   // the unrolled tile loop, the compiler can tell that the transpose reads of one stage do
@@ -191,8 +406,7 @@ __device__ __forceinline__ void win_attn_bf16_item(const uint16_t* __restrict__ 
   // it (the DMA destinations) in scalar registers: 10 fewer VGPRs at D = 128 and no
   // readfirstlane before each DMA.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
+  const LN ln(lane, wave);
 
   const TileId tile = decode_tile(p, item, total);
   const int64_t base = int64_t(tile.bh) * p.head_stride;
@@ -214,15 +428,6 @@ __device__ __forceinline__ void win_attn_bf16_item(const uint16_t* __restrict__ 
   const __amdgpu_buffer_rsrc_t kmrs = make_rsrc(static_cast<const uint16_t*>(p.kmem) + mem_base, mem_bytes);
   const __amdgpu_buffer_rsrc_t vmrs = make_rsrc(static_cast<const uint16_t*>(p.vmem) + mem_base, mem_bytes);
 
-  // ---- K/V tile loads: wave `wave` fills row groups wave*LOADS .. +LOADS-1 of both tiles.
-  // Lane j moves 16 bytes: chunk slot j / RPG of row (group*RPG + j % RPG).
-  const int ld_slot = lane / RPG;
-  const int ld_row = lane % RPG;
-  const uint32_t k_chunk_off = uint32_t(ld_slot) * 16u;
-  const uint32_t v_chunk_off = uint32_t(L::v_slot(ld_slot)) * 16u;
-  // row of its group that the lane loads for V (differs from ld_row only for the upper-half
-  // chunks of D = 64; see TileLayout)
-  const int v_ld_row = (L::V_ROW_SWIZZLE && ld_slot >= CPR / 2) ? (ld_row ^ 4) : ld_row;
   // Byte offset of a window row in the head (rows past the window get an offset beyond the
   // buffer range, so they read as zeros).
   auto row_offset = [&](int local) __attribute__((always_inline)) -> uint32_t {
@@ -239,6 +444,7 @@ __device__ __forceinline__ void win_attn_bf16_item(const uint16_t* __restrict__ 
     const int j = (t - Tw - Tr) * BN + r;
     return j < p.n_mem ? uint32_t(j) * uint32_t(L::ROW_BYTES) : 0xffffff00u;
   };
+  // ---- K/V tile loads: wave `wave` fills row groups wave*LOADS .. +LOADS-1 of both tiles.
   // row_off: LOADS byte offsets of the lane's K rows, then LOADS of its V rows
   auto dma_tile = [&](const uint32_t* row_off, char* st, int t) __attribute__((always_inline)) {
     const bool mem = EXT && t >= Tw + Tr;
@@ -247,8 +453,8 @@ __device__ __forceinline__ void win_attn_bf16_item(const uint16_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int g = wave * C::LOADS + i;
-      dma16_to_lds(ks, st + g * RG, row_off[i] + k_chunk_off);
-      dma16_to_lds(vs, st + C::TILE_BYTES + g * RG, row_off[C::LOADS + i] + v_chunk_off);
+      dma16_to_lds(ks, st + g * RG, row_off[i] + ln.k_chunk_off);
+      dma16_to_lds(vs, st + C::TILE_BYTES + g * RG, row_off[C::LOADS + i] + ln.v_chunk_off);
     }
   };
   // The row offsets of the K/V tiles are computed cooperatively a few tiles ahead into a
@@ -267,9 +473,9 @@ __device__ __forceinline__ void win_attn_bf16_item(const uint16_t* __restrict__ 
   auto read_offs = [&](int t, uint32_t* row_off) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-      row_off[i] = rowtab[(t % TAB_TILES) * BN + (wave * C::LOADS + i) * RPG + ld_row];
+      row_off[i] = rowtab[(t % TAB_TILES) * BN + (wave * C::LOADS + i) * RPG + ln.ld_row];
       if constexpr (L::V_ROW_SWIZZLE)
-        row_off[C::LOADS + i] = rowtab[(t % TAB_TILES) * BN + (wave * C::LOADS + i) * RPG + v_ld_row];
+        row_off[C::LOADS + i] = rowtab[(t % TAB_TILES) * BN + (wave * C::LOADS + i) * RPG + ln.v_ld_row];
       else
         row_off[C::LOADS + i] = row_off[i];
     }
@@ -279,8 +485,8 @@ __device__ __forceinline__ void win_attn_bf16_item(const uint16_t* __restrict__ 
     uint32_t off0[2 * C::LOADS];
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-      off0[i] = row_offset((wave * C::LOADS + i) * RPG + ld_row);
-      off0[C::LOADS + i] = row_offset((wave * C::LOADS + i) * RPG + v_ld_row);
+      off0[i] = row_offset((wave * C::LOADS + i) * RPG + ln.ld_row);
+      off0[C::LOADS + i] = row_offset((wave * C::LOADS + i) * RPG + ln.v_ld_row);
     }
     dma_tile(off0, stage0, 0);
   }
@@ -290,7 +496,6 @@ __device__ __forceinline__ void win_attn_bf16_item(const uint16_t* __restrict__ 
   // rows per wave-wide load), and after the prologue barrier reads its fragments from there.
   // Q is read once per workgroup: non-temporal loads keep it out of the way of the K/V in L2.
   // qrowtab keeps the byte offset of every query row for the output stores.
-  constexpr int QG = 32 / RPG;  // row groups per wave
   __shared__ __attribute__((aligned(1024))) char qbuf[NW * QG * RG];
   __shared__ uint32_t qrowtab[BM];
   {
@@ -298,40 +503,11 @@ __device__ __forceinline__ void win_attn_bf16_item(const uint16_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < QG; ++i) {
       const int g = wave * QG + i;
-      dma16_to_lds<kCachePolicyNT>(qrs, qbuf + g * RG, row_offset(tile.qtile * BM + g * RPG + ld_row) + k_chunk_off);
+      dma16_to_lds<kCachePolicyNT>(qrs, qbuf + g * RG, row_offset(tile.qtile * BM + g * RPG + ln.ld_row) + ln.k_chunk_off);
     }
     if (tid < BM) qrowtab[tid] = row_offset(tile.qtile * BM + tid);
   }
-  // B operand of S^T: lane holds d = hh*D/2 + 8*kk .. +7 of query row wave*32 + l32
-  const int qrow = wave * 32 + l32;
-  const int q_rd = (qrow / RPG) * RG + (qrow % RPG) * 16 + hh * (CPR / 2) * CS;
   bf16x8_t qf[DK];
-
-  // ---- per-lane LDS read bases (all per-step offsets below are compile-time constants)
-  // K (A operand of S^T): row 32*kb + key_perm(l32), chunk hh*CPR/2 + kk.
-  const int krow = key_perm(l32);
-  const int k_rd = (krow / RPG) * RG + (krow % RPG) * 16 + hh * (CPR / 2) * CS;
-  // V^T (A operand of O^T) by transpose reads: in each 16-lane group lane i supplies the
-  // address of 4 consecutive d of key row (i / 4) and receives one d of 4 keys. Lane
-  // (g, i, hh) of block db reads d-chunk 2*db + g (lower half of d) for i%4 in {0, 2} and
-  // CPR/2 + 2*db + g (upper half) for i%4 in {1, 3}; i%4 in {2, 3} take the chunk's upper 8 bytes.
-  const int vg = l32 >> 4;
-  const int vi = lane & 15;
-  const int v_chunk = ((vi & 1) ? CPR / 2 : 0) + vg;           // + 2*db per block
-  // per d block: the slot of chunk v_chunk + 2*db, less the 2*db*CS added at each read.
-  // v_rd1 is the base of the second read (rows +4): with the D = 64 row swizzle the
-  // upper-half lanes find rows 0-3 at positions 4-7 and rows 4-7 at positions 0-3.
-  const bool v_swz = L::V_ROW_SWIZZLE && (vi & 1);
-  int v_rd[DB], v_rd1[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    v_rd[db] = ((8 * hh) / RPG) * RG + ((8 * hh) % RPG + (vi >> 2) + (v_swz ? 4 : 0)) * 16 +
-               (L::v_slot(v_chunk + 2 * db) - 2 * db) * CS + ((vi >> 1) & 1) * 8;
-    v_rd1[db] = v_rd[db] - (v_swz ? 128 : 0);
-  }
-
-  auto acc_key = [&](int kb, int r) { return 32 * kb + key_perm(8 * (r >> 2) + 4 * hh + (r & 3)); };
-
   f32x16_t oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -349,148 +525,37 @@ __device__ __forceinline__ void win_attn_bf16_item(const uint16_t* __restrict__ 
     // refill the ring slots of tiles t-8 .. t-1 (all issued) with tiles t+8 .. t+15, first
     // needed by the DMA of step t+7; the barrier ending this step publishes them
     if (t % REFILL == 0 && t >= REFILL && t + REFILL < Tn) fill_tab(t + REFILL, min(REFILL, Tn - t - REFILL));
-    const char* ks = cur;
-    const char* vs = cur + C::TILE_BYTES;
-
-    // S^T = K Q^T for 64 keys (two 32-key blocks)
-    f32x16_t sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
-    bf16x8_t kf[DK][2];
-#pragma unroll
-    for (int kk = 0; kk < DK; ++kk)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        kf[kk][kb] = *reinterpret_cast<const bf16x8_t*>(ks + k_rd + kb * (32 / RPG) * RG + kk * CS);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kk = 0; kk < DK; ++kk)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk][kb], qf[kk], sacc[kb], 0, 0, 0);
-
-    // ragged last tile of the window, the routed window or the memory: keys past the end
-    // get -inf
+    // ragged last tile of the window, the routed window or the memory
     const int lim = !EXT || t < Tw ? p.wtok - t * BN : t < Tw + Tr ? p.wtok - (t - Tw) * BN : p.n_mem - (t - Tw - Tr) * BN;
-    if (lim < BN) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (acc_key(kb, r) >= lim) sacc[kb][r] = -__builtin_inff();
-    }
-
-    // online softmax (fp32), P^T packed to bf16 as the B operand of O^T += V^T P^T
+    f32x16_t sacc[2];
     bf16x8_t pf[4];
-    {
-      float mx = sacc[0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = wave_half_max(mx) * c;
-      const bool need = mx > m_run + 8.0f;
-      if (__builtin_amdgcn_ballot_w64(need) != 0) {
-        const float m_new = need ? mx : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      }
-      const float neg_m = -m_run;
-      float lsum = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch) {
-          u32x4_t packed;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * ch + 2 * e], c, neg_m));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * ch + 2 * e + 1], c, neg_m));
-            // The row sum adds the bf16-rounded p that the PV product uses. The packed word
-            // goes through a scalar temporary: bit-casting the vector element directly
-            // (packed[e]) makes hipcc 7.2 feed the same register to every v_dot2c.
-            const uint32_t w = pack_bf16x2(p0, p1);
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
-                                                  __builtin_bit_cast(bf16x2_t, 0x3f803f80u), lsum, false);
-            packed[e] = w;
-          }
-          pf[kb * 2 + ch] = __builtin_bit_cast(bf16x8_t, packed);
-        }
-      }
-      l_run += lsum;
-    }
-
-    // O^T += V^T P^T; the 16 keys of chunk (kb, ch) are rows 32kb + 16ch + 8hh + 0..7
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const char* a0 = vs + v_rd[db] + ((32 * kb + 16 * ch) / RPG) * RG + 2 * db * CS;
-          const char* a1 = vs + v_rd1[db] + ((32 * kb + 16 * ch + 4) / RPG) * RG + ((32 * kb + 16 * ch + 4) % RPG) * 16 -
-                           ((32 * kb + 16 * ch) % RPG) * 16 + 2 * db * CS;
-          const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)a0);
-          const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)a1);
-          const bf16x8_t vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb * 2 + ch], oacc[db], 0, 0, 0);
-        }
-      }
-    }
+    ln.s_products(cur, qf, sacc);
+    ln.softmax(lim, c, sacc, pf, m_run, l_run, oacc);
+    ln.pv_products(cur + C::TILE_BYTES, pf, oacc);
     __syncthreads();  // next tile resident; everyone is done with this stage
   };
 
   __syncthreads();  // tile 0 and Q resident, row tables written
-#pragma unroll
-  for (int kk = 0; kk < DK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qbuf + q_rd + kk * CS);
+  ln.load_q(qbuf, qf);
   if (1 < Tn) read_offs(1, next_off);
   for (int t = 0; t < Tn; t += 2) {
     tile_step(t, stage0, stage1);
     if (t + 1 < Tn) tile_step(t + 1, stage1, stage0);
   }
 
-  // ---- normalise and store each row at its original (un-shifted) position. The packed rows
-  // go through this wave's part of the Q buffer, so that each wave-wide store writes RPG
-  // whole rows (16 lanes per 256-byte row) instead of 16 bytes of 64 different rows.
-  {
-    const float l = wave_half_sum(l_run);
-    const float inv = 1.0f / l;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        u32x4_t w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w[e] = pack_bf16x2(oacc[db][8 * half + 2 * e] * inv, oacc[db][8 * half + 2 * e + 1] * inv);
-        // chunk hh*CPR/2 + 2*db + half of row qrow
-        *reinterpret_cast<u32x4_t*>(qbuf + q_rd + (2 * db + half) * CS) = w;
-      }
-    const __amdgpu_buffer_rsrc_t ors = make_rsrc(out + base, head_bytes);
-    u32x4_t w[QG];
-#pragma unroll
-    for (int i = 0; i < QG; ++i)
-      w[i] = *reinterpret_cast<const u32x4_t*>(qbuf + (wave * QG + i) * RG + ld_slot * CS + ld_row * 16);
-#pragma unroll
-    for (int i = 0; i < QG; ++i)
-      buffer_store16(ors, qrowtab[(wave * QG + i) * RPG + ld_row] + k_chunk_off, w[i]);
-    // log-sum-exp of the row's scaled logits, natural log: (m + log2 l) * ln 2
-    if (p.lse != nullptr && hh == 0 && tile.qtile * BM + qrow < p.wtok) {
-      const uint32_t tok = qrowtab[qrow] / uint32_t(L::ROW_BYTES);
-      p.lse[int64_t(tile.bh) * p.n_tokens + tok] = (m_run + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
-    }
+  // ---- normalise and store each row at its original (un-shifted) position, staged through
+  // this wave's part of the Q buffer
+  const float l = wave_half_sum(l_run);
+  ln.template store_rows<1>(qbuf, oacc, 1.0f / l, qrowtab, make_rsrc(out + base, head_bytes), wave);
+  // log-sum-exp of the row's scaled logits, natural log: (m + log2 l) * ln 2
+  if (p.lse != nullptr && ln.hh == 0 && tile.qtile * BM + wave * 32 + ln.l32 < p.wtok) {
+    const uint32_t tok = qrowtab[wave * 32 + ln.l32] / uint32_t(L::ROW_BYTES);
+    p.lse[int64_t(tile.bh) * p.n_tokens + tok] = (m_run + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
   }
 }
 
-// The single argument of the two kernels below: the kernel's argument segment is this
-// struct, so the item loop can re-read the parameters from it by address.
+// The single argument of the kernels below: the kernel's argument segment is this struct,
+// so the loops can re-read the parameters from it by address.
 struct Bf16KernelArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -500,24 +565,28 @@ struct Bf16KernelArgs {
   uint32_t total;  // work items
 };
 
-// Both kernels run a persistent grid of (at most) one workgroup per CU that walks the work
-// items blockIdx.x, blockIdx.x + gridDim.x, ... This drops the CU's gap between
-// workgroups, which is a visible share of a 16-tile item.
+// The kernel's parameters, re-read from the argument segment through a pointer the compiler
+// cannot see through: kept in scalar registers across the loops they would spill.
+__device__ __forceinline__ const Bf16KernelArgs& kernel_args() {
+  using ArgPtr = const __attribute__((address_space(4))) Bf16KernelArgs*;
+  ArgPtr ap = (ArgPtr)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(ap));
+  return *(const Bf16KernelArgs*)ap;
+}
+
+// Per-item kernels: a persistent grid of (at most) one workgroup per CU walks the work items
+// blockIdx.x, blockIdx.x + gridDim.x, ... This drops the CU's gap between workgroups, which
+// is a visible share of a 16-tile item.
 template <int D, int NW, bool EXT>
 __device__ __forceinline__ void win_attn_bf16_items(const Bf16KernelArgs& a) {
   for (uint32_t item = blockIdx.x; item < a.total; item += gridDim.x) {
-    // The parameters are read from the argument segment again for each item, through a
-    // pointer the compiler cannot see through; kept in scalar registers across the loop
-    // they would spill.
-    using ArgPtr = const __attribute__((address_space(4))) Bf16KernelArgs*;
-    ArgPtr ap = (ArgPtr)__builtin_amdgcn_kernarg_segment_ptr();
-    asm volatile("" : "+s"(ap));
-    win_attn_bf16_item<D, NW, EXT>(a.q, a.k, a.v, a.out, ((const Bf16KernelArgs*)ap)->p, item, a.total);
+    win_attn_bf16_item<D, NW, EXT>(a.q, a.k, a.v, a.out, kernel_args().p, item, a.total);
     __syncthreads();  // the next item's prologue rewrites LDS the epilogue may still read
   }
 }
 
-// Plain shifted-window attention (§3.1).
+// Plain shifted-window attention (§3.1), one item at a time (small windows, tensors beyond
+// the stream kernel's 32-bit offsets).
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void win_attn_bf16_kernel(
     Bf16KernelArgs a) {
@@ -529,6 +598,216 @@ template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void win_attn_bf16_ext_kernel(
     Bf16KernelArgs a) {
   win_attn_bf16_items<D, NW, true>(a);
+}
+
+// Plain shifted-window attention (§3.1) as one continuous K/V tile stream per workgroup.
+//
+// The persistent workgroup walks items blockIdx.x, blockIdx.x + gridDim.x, ... as one
+// sequence of K/V tiles (global tile g = item sequence number * Tn + tile), so that the work
+// between two items is off the critical path:
+//   * the ring of K/V row offsets runs across items: the refill at step g writes tiles
+//     g+8 .. g+15, which near an item's end belong to the next item;
+//   * the K/V DMA of the last step of an item fetches the next item's first tile;
+//   * the next item's query-row offsets are computed in the first step of an item and its
+//     Q rows DMA'd into the Q buffer over the remaining steps, a few row groups per wave per
+//     step (the Q buffer is free once an item's Q fragments are in registers);
+//   * the output rows are staged through the stage the last tile was read from, in two
+//     passes of 16 rows per wave (the other stage already holds the next item's first tile).
+// Every tensor is addressed through one buffer resource over the whole tensor, with byte
+// offsets bh * head_bytes + token * row_bytes: the launcher uses this kernel only when a
+// tensor fits in 0xffffff00 bytes and every window has at least two K/V tiles (one step
+// computes the next item's query rows, the later ones load them), and only for windows of
+// fewer than 16 key tiles, where the item transitions are a large share of the work.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void win_attn_bf16_stream_kernel(
+    Bf16KernelArgs a) {
+  using C = Bf16Cfg<D, NW>;
+  using L = TileLayout<D>;
+  using LN = Bf16Lane<D, NW>;
+  constexpr int BN = C::BN, BM = C::BM, DK = C::DK, DB = C::DB;
+  constexpr int RPG = L::RPG, RG = L::RG;
+  constexpr int QG = LN::QG;
+  constexpr int TAB_TILES = 16;
+  constexpr int REFILL = 8;
+
+  __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char stage1[C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char qbuf[NW * QG * RG];
+  __shared__ uint32_t rowtab[TAB_TILES * BN];
+  __shared__ uint32_t qrowtab[2][BM];
+  static_assert(NW * (QG / 2) * RG <= C::STAGE_BYTES, "two-pass output staging must fit one stage");
+
+  int tid;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"(int(threadIdx.x)));
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const LN ln(lane, wave);
+
+  const uint32_t total = a.total;
+  const int Tn = a.p.kv_tiles;
+  const int wtok = a.p.wtok;
+  const float c = a.p.scale_log2;
+  const uint32_t head_bytes = uint32_t(a.p.head_stride) * 2u;
+  const uint32_t tensor_bytes = uint32_t(a.p.heads_total) * head_bytes;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k, tensor_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v, tensor_bytes);
+  // Q and out are touched a few times per item: their resources are built where used, from
+  // the re-read arguments, so that they hold no scalar registers across the tile loop
+
+  // Byte offset (in the whole tensor) of row `local` of item `it`'s window; rows past the
+  // window get an offset beyond the resource range (zero reads, dropped writes).
+  auto item_row = [&](uint32_t it, int local) __attribute__((always_inline)) -> uint32_t {
+    const AttnParams& p = kernel_args().p;
+    const TileId tl = decode_tile(p, it, total);
+    const WinOrigin o = window_origin(p.map, uint32_t(tl.win));
+    return local < wtok ? uint32_t(tl.bh) * head_bytes + uint32_t(token_of(p.map, o, uint32_t(local))) * L::ROW_BYTES
+                        : 0xffffff00u;
+  };
+  auto item_qtile = [&](uint32_t it) __attribute__((always_inline)) -> int {
+    return decode_tile(kernel_args().p, it, total).qtile;
+  };
+
+  // this workgroup's items: blockIdx.x + j * gridDim.x, j < n_items; global tiles g < g_end
+  const uint32_t n_items = (total - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  const int g_end = int(n_items) * Tn;
+  uint32_t item = blockIdx.x;  // current item
+  int g0 = 0;                  // global index of its first tile
+  int qb = 0;                  // which qrowtab holds its query-row offsets
+  // Offsets of the rows of ring tile g (global; g < g_end): tile g - j*Tn of item j = g / Tn.
+  auto fill_tile_rows = [&](int g, int row) __attribute__((always_inline)) {
+    const uint32_t j = fdiv(uint32_t(g), kernel_args().p.f_kv_tiles);
+    const int t = g - int(j) * Tn;
+    rowtab[(g % TAB_TILES) * BN + row] = item_row(blockIdx.x + j * gridDim.x, t * BN + row);
+  };
+  auto dma_tile = [&](const uint32_t* row_off, char* st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int g = wave * C::LOADS + i;
+      dma16_to_lds(krs, st + g * RG, row_off[i] + ln.k_chunk_off);
+      dma16_to_lds(vrs, st + C::TILE_BYTES + g * RG, row_off[C::LOADS + i] + ln.v_chunk_off);
+    }
+  };
+  auto read_offs = [&](int g, uint32_t* row_off) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      row_off[i] = rowtab[(g % TAB_TILES) * BN + (wave * C::LOADS + i) * RPG + ln.ld_row];
+      if constexpr (L::V_ROW_SWIZZLE)
+        row_off[C::LOADS + i] = rowtab[(g % TAB_TILES) * BN + (wave * C::LOADS + i) * RPG + ln.v_ld_row];
+      else
+        row_off[C::LOADS + i] = row_off[i];
+    }
+  };
+  auto dma_q = [&](int grp, const uint32_t* qrow) __attribute__((always_inline)) {
+    const int g = wave * QG + grp;
+    dma16_to_lds<kCachePolicyNT>(make_rsrc(kernel_args().q, tensor_bytes), qbuf + g * RG,
+                                 qrow[g * RPG + ln.ld_row] + ln.k_chunk_off);
+  };
+
+  // ---- prologue: ring tiles 0 .. 15 and the first item's query rows
+  static_assert(BN == 64, "one ring tile per wave-wide fill");
+  for (int tt = wave; tt < TAB_TILES; tt += NW)
+    if (tt < g_end) fill_tile_rows(tt, lane);
+  {
+    const int qt = item_qtile(item);
+    if (tid < BM) qrowtab[0][tid] = item_row(item, qt * BM + tid);
+  }
+  __syncthreads();
+  uint32_t next_off[2 * C::LOADS];
+  read_offs(0, next_off);
+  dma_tile(next_off, stage0);
+#pragma unroll
+  for (int i = 0; i < QG; ++i) dma_q(i, qrowtab[0]);
+  if (1 < g_end) read_offs(1, next_off);
+  __syncthreads();  // tile 0 and Q resident
+
+  bf16x8_t qf[DK];
+  ln.load_q(qbuf, qf);
+  f32x16_t oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+  float m_run = -__builtin_inff(), l_run = 0.0f;
+
+  // Work of a few steps per item (the ring refill every REFILL steps; the next item's query
+  // rows in its first steps): out of line, so that the common step runs straight through.
+  // The last step of an item that loads the next item's Q rows.
+  const int q_steps = Tn - 1 < QG ? Tn - 1 : QG;
+  auto rare_work = [&](int g, int t) __attribute__((always_inline)) {
+    // refill the ring slots of tiles g-8 .. g-1 (all issued) with tiles g+8 .. g+15 that
+    // exist; first needed by the DMA of step g+7, published by this step's barrier
+    if (g % REFILL == 0 && g >= REFILL) {
+      for (int w = wave; w < REFILL; w += NW) {
+        const int gt = g + REFILL + w;
+        if (gt < g_end) fill_tile_rows(gt, lane);
+      }
+    }
+    if (g0 + Tn < g_end && t <= q_steps) {  // a next item exists
+      if (t == 0) {
+        // query-row offsets of the next item (its stores and its Q loads read them)
+        const uint32_t nx = item + gridDim.x;
+        const int qt = item_qtile(nx);
+        if (tid < BM) qrowtab[qb ^ 1][tid] = item_row(nx, qt * BM + tid);
+      } else {
+        // its Q rows, qps row groups per wave in each of steps 1 .. q_steps
+        const int qps = (QG + q_steps - 1) / q_steps;
+        for (int i = (t - 1) * qps; i < min(t * qps, QG); ++i) dma_q(i, qrowtab[qb ^ 1]);
+      }
+    }
+  };
+
+  // One step of the stream: compute global tile g from `cur`, prefetch tile g+1 into `nxt`.
+  // Returns true when g was the last tile of the current item.
+  auto step = [&](int g, const char* cur, char* nxt) __attribute__((always_inline)) -> bool {
+    const int t = g - g0;
+    if (__builtin_expect(g + 1 < g_end, 1)) dma_tile(next_off, nxt);
+    if (__builtin_expect((g % REFILL == 0 && g >= REFILL) || (g0 + Tn < g_end && t <= q_steps), 0)) rare_work(g, t);
+    // Scalar loads the compiler issues above (parameters it re-reads instead of keeping them
+    // in registers) return out of order with LDS reads; with one in flight, every wait for
+    // the K fragments below would have to be a wait for all of them. Draining here lets the
+    // S products start as soon as their first fragments arrive.
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    if (__builtin_expect(g + 2 < g_end, 1)) read_offs(g + 2, next_off);
+    f32x16_t sacc[2];
+    bf16x8_t pf[4];
+    ln.s_products(cur, qf, sacc);
+    ln.softmax(wtok - t * BN, c, sacc, pf, m_run, l_run, oacc);
+    ln.pv_products(cur + C::TILE_BYTES, pf, oacc);
+    __syncthreads();  // tile g+1 resident; everyone is done with this stage
+    return __builtin_expect(t + 1 == Tn, 0);
+  };
+  // End of an item: normalise and store its rows through `cur` (free after the last step's
+  // barrier), then start the next item. Returns false when there is none.
+  auto finish_item = [&](char* cur) __attribute__((always_inline)) -> bool {
+    ln.template store_rows<2>(cur, oacc, 1.0f / wave_half_sum(l_run), qrowtab[qb],
+                              make_rsrc(kernel_args().out, tensor_bytes), wave);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+    m_run = -__builtin_inff();
+    l_run = 0.0f;
+    if (g0 >= g_end) return false;
+    item += gridDim.x;
+    qb ^= 1;
+    // the staging reads of `cur` are done before the next step's DMA rewrites it; the next
+    // item's Q has been in the Q buffer since the first steps of this item. The barrier does
+    // not wait for the output stores.
+    lds_barrier();
+    ln.load_q(qbuf, qf);
+    return true;
+  };
+
+  for (int g = 0;; g += 2) {
+    if (step(g, stage0, stage1)) {
+      g0 = g + 1;
+      if (!finish_item(stage0)) break;
+    }
+    if (step(g + 1, stage1, stage0)) {
+      g0 = g + 2;
+      if (!finish_item(stage1)) break;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------------
@@ -988,6 +1267,7 @@ static hipError_t launch_bf16(const void* q, const void* k, const void* v, void*
   using C = Bf16Cfg<D, NW>;
   p.q_tiles = (p.wtok + C::BM - 1) / C::BM;
   p.kv_tiles = (p.wtok + C::BN - 1) / C::BN;
+  p.f_kv_tiles = make_fastdiv(uint32_t(p.kv_tiles));
   p.mem_tiles = (p.n_mem + C::BN - 1) / C::BN;
   const uint64_t blocks = uint64_t(p.q_tiles) * uint64_t(p.n_win) * uint64_t(p.heads_total);
   if (blocks == 0 || blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
@@ -1002,8 +1282,18 @@ static hipError_t launch_bf16(const void* q, const void* k, const void* v, void*
   const hipError_t e = persistent_slots(&slots);
   if (e != hipSuccess) return e;
   const uint32_t grid = blocks < slots ? uint32_t(blocks) : slots;
-  if (p.route != nullptr || p.n_mem > 0)
+  // The stream kernel pays for its cross-item prefetch with a few scalar instructions and
+  // branches in every step; it is the faster one for windows of fewer than 16 key tiles
+  // (measured: FLUX-1024, 4 tiles, 4 % faster; 16 tiles and more, 1-3 % slower; dense 3-9 %
+  // slower). It addresses a whole tensor through one 32-bit buffer range (rows past a
+  // window at offsets from 0xffffff00 up), needs at least two K/V tiles per window and
+  // numbers a workgroup's tiles with 32-bit integers.
+  const uint64_t tensor_bytes = uint64_t(p.heads_total) * uint64_t(p.head_stride) * 2u;
+  const uint64_t wg_tiles = (blocks + grid - 1) / grid * uint64_t(p.kv_tiles);
+  if (p.route != nullptr || p.n_mem > 0 || p.lse != nullptr)
     hipLaunchKernelGGL((win_attn_bf16_ext_kernel<D, NW>), dim3(grid), dim3(C::NT), 0, stream, a);
+  else if (p.kv_tiles >= 2 && p.kv_tiles < 16 && tensor_bytes <= 0xffffff00u && wg_tiles < 0x7fffffffu)
+    hipLaunchKernelGGL((win_attn_bf16_stream_kernel<D, NW>), dim3(grid), dim3(C::NT), 0, stream, a);
   else
     hipLaunchKernelGGL((win_attn_bf16_kernel<D, NW>), dim3(grid), dim3(C::NT), 0, stream, a);
   return hipGetLastError();

@@ -31,6 +31,9 @@ CASES = [
     ("plain-d64-ragged", 1, 80, 64, (2, 20, 30), (2, 10, 15), (1, 4, -6), "plain", None, 302),
     ("memory-d128", 1, 100, 128, (1, 32, 32), (1, 8, 16), (0, 4, 8), "memory", (4, 4), 303),
     ("routed-memory-d64", 1, 100, 64, (1, 32, 32), (1, 8, 16), (0, 5, 3), "routed+memory", (4, 4), 304),
+    # windows of 8 and 15 key tiles (2 and 4 query tiles): the continuous-stream kernel
+    ("plain-d128-w512", 1, 80, 128, (1, 32, 64), (1, 16, 32), (0, 5, 9), "plain", None, 305),
+    ("plain-d128-w960-ragged", 1, 40, 128, (1, 48, 80), (1, 24, 40), (0, 7, -11), "plain", None, 306),
 ]
 
 
