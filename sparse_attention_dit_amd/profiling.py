@@ -37,11 +37,32 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 ATTN_KERNEL = "win_attn_bf16_kernel"
+STREAM_KERNEL = "win_attn_bf16_stream_kernel"
+F32_KERNEL = "win_attn_f32_kernel"
 COPY_BYTES = 256 << 20  # calibration copy: 256 MiB read + 256 MiB written per launch
 
 
+def kernel_name(dtype: str, window_tokens: int) -> str:
+    """The kernel the library launches for plain windowed attention over windows of
+    `window_tokens` (the dense baseline: the whole sequence). Mirrors the launcher: fp32
+    inputs run the fp32 kernel; bf16 windows of 2 to 15 key tiles of 64 run the stream
+    kernel, all others the per-item kernel."""
+    if dtype != "bf16":
+        return F32_KERNEL
+    tiles = -(-window_tokens // 64)
+    return STREAM_KERNEL if 2 <= tiles < 16 else ATTN_KERNEL
+
+
 def traffic_json_name(workload: str) -> str:
-    return f"{ATTN_KERNEL}.{workload}.traffic.json"
+    from sparse_attention_dit_amd.configs import BY_NAME
+    w = BY_NAME[workload]
+    return f"{kernel_name(w.dtype, w.window_tokens)}.{workload}.traffic.json"
+
+
+def _matches(kernel_field: str, kernel: str) -> bool:
+    """rocprofv3 kernel names are demangled signatures; match the function name exactly
+    (the per-item kernel's name is a prefix of neither of the others)."""
+    return f"::{kernel}<" in kernel_field or kernel_field.startswith(kernel + "<") or f" {kernel}<" in kernel_field
 
 
 # ------------------------------------------------------------------ profiled program
@@ -86,23 +107,26 @@ def _find_csv(directory: str, suffix: str) -> str:
     return hits[0]
 
 
-def _kernel_rows(directory: str):
-    """Dispatches of the attention kernel from a kernel-trace CSV, in dispatch order."""
+def _kernel_rows(directory: str, kernels=(ATTN_KERNEL,)):
+    """Dispatches of the given attention kernels from a kernel-trace CSV, in dispatch order."""
     rows = []
     with open(_find_csv(directory, "kernel_trace.csv")) as f:
         for r in csv.DictReader(f):
-            if ATTN_KERNEL in r["Kernel_Name"]:
+            if any(_matches(r["Kernel_Name"], k) for k in kernels):
                 rows.append(r)
     rows.sort(key=lambda r: int(r["Dispatch_Id"]))
     return rows
 
 
-def _counter_per_dispatch(directory: str, counter: str, kernel_substr: str, grid: int | None = None):
-    """Mean and count of a counter's per-dispatch value over the matching dispatches."""
+def _counter_per_dispatch(directory: str, counter: str, kernel_substr: str, grid: int | None = None,
+                          exact: bool = True):
+    """Mean and count of a counter's per-dispatch value over the matching dispatches (kernel
+    function named exactly, or with exact=False any kernel whose name contains the text)."""
     vals = []
     with open(_find_csv(directory, "counter_collection.csv")) as f:
         for r in csv.DictReader(f):
-            if r["Counter_Name"] != counter or kernel_substr not in r["Kernel_Name"]:
+            name_ok = _matches(r["Kernel_Name"], kernel_substr) if exact else kernel_substr in r["Kernel_Name"]
+            if r["Counter_Name"] != counter or not name_ok:
                 continue
             if grid is not None and int(r["Grid_Size"]) != grid:
                 continue
@@ -120,14 +144,27 @@ def _stats_table(durations_ns):
 
 # ------------------------------------------------------------------ summaries
 def _kernel_stats(directory: str, dense: int, cmd: str, out: str, bench_json: str | None) -> None:
-    rows = _kernel_rows(directory)
-    if len(rows) <= dense:
-        raise ValueError(f"{len(rows)} attention dispatches, expected more than {dense}")
-    dur = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows]
-    win, full = _stats_table(dur[:-dense]), _stats_table(dur[-dense:])
-    name = rows[0]["Kernel_Name"]
-    lines = [f"# Kernel trace: {ATTN_KERNEL}", "", "Command (from the repository root):", "", "```", cmd, "```", "",
-             f"Kernel: `{name[:120]}`", "",
+    win_kernel = dense_kernel = ATTN_KERNEL
+    if bench_json:
+        from sparse_attention_dit_amd.configs import BY_NAME
+        with open(bench_json) as f:
+            wl = BY_NAME[json.loads(f.read().strip().splitlines()[-1])["config"]["workload"]]
+        win_kernel, dense_kernel = kernel_name(wl.dtype, wl.window_tokens), kernel_name(wl.dtype, wl.tokens)
+    if win_kernel == dense_kernel:
+        # one kernel: bench.py's dense launches come last (2 untimed + --full-iters timed)
+        rows = _kernel_rows(directory, (win_kernel,))
+        if len(rows) <= dense:
+            raise ValueError(f"{len(rows)} attention dispatches, expected more than {dense}")
+        win_rows, dense_rows = rows[:-dense], rows[-dense:]
+    else:
+        win_rows, dense_rows = _kernel_rows(directory, (win_kernel,)), _kernel_rows(directory, (dense_kernel,))
+    dur = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in win_rows]
+    win = _stats_table(dur)
+    full = _stats_table([int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in dense_rows])
+    name = win_rows[0]["Kernel_Name"]
+    lines = [f"# Kernel trace: {win_kernel}", "", "Command (from the repository root):", "", "```", cmd, "```", "",
+             f"Kernel: `{name[:120]}`" + ("" if win_kernel == dense_kernel else
+                                          f"; dense baseline: `{dense_rows[0]['Kernel_Name'][:120]}`"), "",
              "| launches | calls | avg µs | median µs | min µs | max µs |", "|---|---|---|---|---|---|"]
     for label, s in (("windowed (all of bench.py's windowed launches)", win), ("dense baseline", full)):
         lines.append(f"| {label} | {s['calls']} | {s['avg_us']:.2f} | {s['median_us']:.2f} | {s['min_us']:.2f} | "
@@ -190,11 +227,12 @@ def _traffic(a) -> None:
     from sparse_attention_dit_amd.configs import BY_NAME
 
     w = BY_NAME[a.workload]
-    fetch_kib, n_f = _counter_per_dispatch(a.fetch, "FETCH_SIZE", ATTN_KERNEL)
-    write_kib, n_w = _counter_per_dispatch(a.write, "WRITE_SIZE", ATTN_KERNEL)
+    kernel = kernel_name(w.dtype, w.window_tokens)
+    fetch_kib, n_f = _counter_per_dispatch(a.fetch, "FETCH_SIZE", kernel)
+    write_kib, n_w = _counter_per_dispatch(a.write, "WRITE_SIZE", kernel)
     # the copy program's device-to-device copy runs as the runtime's copy kernel
-    cf_kib, n_cf = _counter_per_dispatch(a.copy_fetch, "FETCH_SIZE", a.copy_kernel)
-    cw_kib, n_cw = _counter_per_dispatch(a.copy_write, "WRITE_SIZE", a.copy_kernel)
+    cf_kib, n_cf = _counter_per_dispatch(a.copy_fetch, "FETCH_SIZE", a.copy_kernel, exact=False)
+    cw_kib, n_cw = _counter_per_dispatch(a.copy_write, "WRITE_SIZE", a.copy_kernel, exact=False)
     f_scale = COPY_BYTES / (cf_kib * 1024.0)
     w_scale = COPY_BYTES / (cw_kib * 1024.0)
     fetch_b = fetch_kib * 1024.0 * f_scale
@@ -202,7 +240,7 @@ def _traffic(a) -> None:
     algo = w.io_bytes()
     rec = {
         "workload": w.name,
-        "kernel": ATTN_KERNEL,
+        "kernel": kernel,
         "kernel_hash": kernel_hash(),
         "hbm_bytes_per_launch": round(fetch_b + write_b),
         "fetch_bytes_per_launch": round(fetch_b),
@@ -221,7 +259,7 @@ def _traffic(a) -> None:
     with open(jpath, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
-    md = [f"# HBM traffic of {ATTN_KERNEL}, workload {w.name}", "",
+    md = [f"# HBM traffic of {kernel}, workload {w.name}", "",
           "Commands (from the repository root; one rocprofv3 counter pass each):", "", "```", *a.cmd, "```", "",
           "| quantity | value |", "|---|---|",
           f"| FETCH_SIZE per dispatch (KiB, mean of {n_f}) | {fetch_kib:.1f} |",
@@ -233,7 +271,7 @@ def _traffic(a) -> None:
           f"| algorithmic bytes per launch (q, k, v read once, out written once) | {algo / 1e6:.2f} MB |",
           f"| traffic / algorithmic | {(fetch_b + write_b) / algo:.3f} |",
           "", f"Kernel source digest: `{rec['kernel_hash']}`"]
-    mpath = os.path.join(a.out_dir, f"{ATTN_KERNEL}.{w.name}.traffic.md")
+    mpath = os.path.join(a.out_dir, f"{kernel}.{w.name}.traffic.md")
     with open(mpath, "w") as f:
         f.write("\n".join(md) + "\n")
     print(f"wrote {jpath} and {mpath}: {(fetch_b + write_b) / 1e6:.2f} MB per launch "
@@ -258,6 +296,8 @@ def _counters(a) -> None:
     from sparse_attention_dit_amd.configs import BY_NAME
 
     w = BY_NAME[a.workload]
+    if a.kernel is None:
+        a.kernel = kernel_name(w.dtype, w.window_tokens if a.what == "window" else w.tokens)
     vals = {}
     for directory, names in ((a.mfma, COUNTER_PASSES["mfma"]), (a.valu, COUNTER_PASSES["valu"])):
         for n in names:
@@ -343,7 +383,7 @@ def main(argv=None) -> None:
     c.add_argument("--valu", required=True, help="output directory of the 'valu' counter pass")
     c.add_argument("--workload", required=True)
     c.add_argument("--what", choices=("window", "full"), default="window")
-    c.add_argument("--kernel", default=ATTN_KERNEL, help="substring naming the profiled kernel")
+    c.add_argument("--kernel", default=None, help="profiled kernel (default: the one the library launches)")
     c.add_argument("--cmd", action="append", required=True)
     c.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
     a = ap.parse_args(argv)

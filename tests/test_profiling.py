@@ -80,6 +80,7 @@ def test_committed_traffic_records_are_consistent():
         rec = json.load(open(os.path.join(pdir, name)))
         wl = BY_NAME[rec["workload"]]
         assert name == profiling.traffic_json_name(wl.name)
+        assert rec["kernel"] == profiling.kernel_name(wl.dtype, wl.window_tokens)
         assert rec["algorithmic_bytes_per_launch"] == wl.io_bytes()
         assert rec["hbm_bytes_per_launch"] == rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
 
@@ -153,3 +154,20 @@ def test_host_info_fields():
     assert info["logical_cpus_available"] >= 1
     assert info["numpy"]
     assert set(info) == {"cpu_model", "logical_cpus_available", "physical_cores", "numpy", "blas"}
+
+
+def test_kernel_choice_mirrors_the_launcher():
+    """The profile summaries name the kernel the library launches for a workload: fp32 inputs
+    the fp32 kernel, bf16 windows of 2-15 key tiles of 64 the stream kernel, else the per-item
+    kernel (the launcher's rule in attn_kernels.hip)."""
+    assert profiling.kernel_name("f32", 64) == "win_attn_f32_kernel"
+    assert profiling.kernel_name("bf16", 64) == "win_attn_bf16_kernel"
+    assert profiling.kernel_name("bf16", 65) == "win_attn_bf16_stream_kernel"
+    assert profiling.kernel_name("bf16", 256) == "win_attn_bf16_stream_kernel"
+    assert profiling.kernel_name("bf16", 960) == "win_attn_bf16_stream_kernel"
+    assert profiling.kernel_name("bf16", 1024) == "win_attn_bf16_kernel"
+    assert profiling._matches("void basa::win_attn_bf16_stream_kernel<128, 8>(basa::Bf16KernelArgs)",
+                              "win_attn_bf16_stream_kernel")
+    assert not profiling._matches("void basa::win_attn_bf16_stream_kernel<128, 8>(basa::Bf16KernelArgs)",
+                                  "win_attn_bf16_kernel")
+    assert profiling._matches("void basa::win_attn_bf16_kernel<128, 8>(basa::Bf16KernelArgs)", "win_attn_bf16_kernel")
