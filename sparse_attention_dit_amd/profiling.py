@@ -53,10 +53,12 @@ def kernel_name(dtype: str, window_tokens: int) -> str:
     return STREAM_KERNEL if 2 <= tiles < 16 else ATTN_KERNEL
 
 
-def traffic_json_name(workload: str) -> str:
+def traffic_json_name(workload: str, tag: str = "") -> str:
+    """File name of the traffic record of a workload's windowed kernel; `tag` (e.g. "cold")
+    names a record taken under other cache conditions."""
     from sparse_attention_dit_amd.configs import BY_NAME
     w = BY_NAME[workload]
-    return f"{kernel_name(w.dtype, w.window_tokens)}.{workload}.traffic.json"
+    return f"{kernel_name(w.dtype, w.window_tokens)}.{workload}.{tag + '.' if tag else ''}traffic.json"
 
 
 def _matches(kernel_field: str, kernel: str) -> bool:
@@ -66,7 +68,7 @@ def _matches(kernel_field: str, kernel: str) -> bool:
 
 
 # ------------------------------------------------------------------ profiled program
-def _run(what: str, workload: str, iters: int) -> None:
+def _run(what: str, workload: str, iters: int, cold: bool = False) -> None:
     import numpy as np
     import torch
 
@@ -89,14 +91,20 @@ def _run(what: str, workload: str, iters: int) -> None:
     else:
         dev = {n: torch.from_numpy(t.dev[n]).to("cuda") for n in "qkv"}
     out = torch.empty_like(dev["q"])
+    # cold: a 1 GiB write before every launch evicts q, k and v from the L2s and the MALL
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if cold else None
+    n = 0
     for _ in range(iters):
-        if what == "window":
-            for s in w.shifts:
+        for s in (w.shifts if what == "window" else [None]):
+            if flush is not None:
+                flush.fill_(n & 0xFF)
+            n += 1
+            if what == "window":
                 _lib.window_attn_fwd(dev["q"], dev["k"], dev["v"], out, w.grid, w.window, s)
-        else:
-            _lib.full_attn_fwd(dev["q"], dev["k"], dev["v"], out)
+            else:
+                _lib.full_attn_fwd(dev["q"], dev["k"], dev["v"], out)
     torch.cuda.synchronize()
-    print(f"{what}: {workload}, {iters} iterations", flush=True)
+    print(f"{what}: {workload}, {iters} iterations{' (cold)' if cold else ''}", flush=True)
 
 
 # ------------------------------------------------------------------ CSV readers
@@ -252,14 +260,17 @@ def _traffic(a) -> None:
         "dispatches": {"fetch": n_f, "write": n_w, "copy_fetch": n_cf, "copy_write": n_cw},
         "copy_bytes": COPY_BYTES,
         "scale": {"fetch": round(f_scale, 5), "write": round(w_scale, 5)},
+        "caches": "cold: 1 GiB written before each launch" if a.tag == "cold" else "as left by the previous launch",
+        "tag": a.tag,
         "commands": a.cmd,
     }
     os.makedirs(a.out_dir, exist_ok=True)
-    jpath = os.path.join(a.out_dir, traffic_json_name(w.name))
+    jpath = os.path.join(a.out_dir, traffic_json_name(w.name, a.tag))
     with open(jpath, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
-    md = [f"# HBM traffic of {kernel}, workload {w.name}", "",
+    md = [f"# HBM traffic of {kernel}, workload {w.name}{' (' + a.tag + ')' if a.tag else ''}", "",
+          f"Caches: {rec['caches']}.", "",
           "Commands (from the repository root; one rocprofv3 counter pass each):", "", "```", *a.cmd, "```", "",
           "| quantity | value |", "|---|---|",
           f"| FETCH_SIZE per dispatch (KiB, mean of {n_f}) | {fetch_kib:.1f} |",
@@ -271,7 +282,7 @@ def _traffic(a) -> None:
           f"| algorithmic bytes per launch (q, k, v read once, out written once) | {algo / 1e6:.2f} MB |",
           f"| traffic / algorithmic | {(fetch_b + write_b) / algo:.3f} |",
           "", f"Kernel source digest: `{rec['kernel_hash']}`"]
-    mpath = os.path.join(a.out_dir, f"{kernel}.{w.name}.traffic.md")
+    mpath = os.path.join(a.out_dir, traffic_json_name(w.name, a.tag)[:-len("json")] + "md")
     with open(mpath, "w") as f:
         f.write("\n".join(md) + "\n")
     print(f"wrote {jpath} and {mpath}: {(fetch_b + write_b) / 1e6:.2f} MB per launch "
@@ -365,6 +376,7 @@ def main(argv=None) -> None:
     r.add_argument("--what", choices=("window", "full", "copy"), required=True)
     r.add_argument("--workload", default="flux-2048-128x128-w32")
     r.add_argument("--iters", type=int, default=4)
+    r.add_argument("--cold", action="store_true", help="write 1 GiB before each launch (HBM-cold caches)")
     k = sub.add_parser("kernel-stats")
     k.add_argument("--dir", required=True)
     k.add_argument("--dense", type=int, default=7, help="number of trailing dense launches bench.py made")
@@ -376,6 +388,7 @@ def main(argv=None) -> None:
         t.add_argument("--" + n.replace("_", "-"), dest=n, required=True)
     t.add_argument("--copy-kernel", default="copyBuffer", help="substring naming the copy kernel")
     t.add_argument("--workload", required=True)
+    t.add_argument("--tag", default="", choices=("", "cold"), help="cache conditions of the counted launches")
     t.add_argument("--cmd", action="append", required=True)
     t.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
     c = sub.add_parser("counters")
@@ -391,7 +404,7 @@ def main(argv=None) -> None:
         _counters(a)
         return
     if a.cmd_name == "run":
-        _run(a.what, a.workload, a.iters)
+        _run(a.what, a.workload, a.iters, a.cold)
     elif a.cmd_name == "kernel-stats":
         _kernel_stats(a.dir, a.dense, a.cmd, a.out, a.bench_json)
     else:

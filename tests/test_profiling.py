@@ -41,11 +41,18 @@ def test_traffic_scaling(tmp_path):
                     "--copy-fetch", str(tmp_path / "cf"), "--copy-write", str(tmp_path / "cw"),
                     "--workload", wl, "--cmd", "cmd", "--out-dir", str(out)])
     rec = json.load(open(out / profiling.traffic_json_name(wl)))
+    assert rec["tag"] == "" and not (out / profiling.traffic_json_name(wl, "cold")).exists()
     assert rec["fetch_bytes_per_launch"] == round(101.0 * 1024 * 2)
     assert rec["write_bytes_per_launch"] == 50 * 1024
     assert rec["hbm_bytes_per_launch"] == rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
     assert rec["algorithmic_bytes_per_launch"] == BY_NAME[wl].io_bytes()
     assert rec["kernel_hash"] == kernel_hash()
+    profiling.main(["traffic", "--fetch", str(tmp_path / "f"), "--write", str(tmp_path / "w"),
+                    "--copy-fetch", str(tmp_path / "cf"), "--copy-write", str(tmp_path / "cw"),
+                    "--workload", wl, "--tag", "cold", "--cmd", "cmd", "--out-dir", str(out)])
+    cold = json.load(open(out / profiling.traffic_json_name(wl, "cold")))
+    assert cold["tag"] == "cold" and cold["hbm_bytes_per_launch"] == rec["hbm_bytes_per_launch"]
+    assert (out / profiling.traffic_json_name(wl, "cold").replace(".json", ".md")).exists()
 
 
 def test_kernel_stats_split(tmp_path):
@@ -79,7 +86,7 @@ def test_committed_traffic_records_are_consistent():
     for name in found:
         rec = json.load(open(os.path.join(pdir, name)))
         wl = BY_NAME[rec["workload"]]
-        assert name == profiling.traffic_json_name(wl.name)
+        assert name == profiling.traffic_json_name(wl.name, rec.get("tag", ""))
         assert rec["kernel"] == profiling.kernel_name(wl.dtype, wl.window_tokens)
         assert rec["algorithmic_bytes_per_launch"] == wl.io_bytes()
         assert rec["hbm_bytes_per_launch"] == rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
