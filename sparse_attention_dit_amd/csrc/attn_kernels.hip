@@ -61,10 +61,11 @@ __device__ __forceinline__ TileId decode_tile(const AttnParams& p, uint32_t bid,
   const uint32_t rem = total % kNumXcd;
   const uint32_t logical = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
   TileId t;
-  t.qtile = int32_t(logical % uint32_t(p.q_tiles));
-  const uint32_t rest = logical / uint32_t(p.q_tiles);
-  t.win = int32_t(rest % uint32_t(p.n_win));
-  t.bh = int32_t(rest / uint32_t(p.n_win));
+  const uint32_t rest = fdiv(logical, p.f_q_tiles);
+  t.qtile = int32_t(logical - rest * uint32_t(p.q_tiles));
+  const uint32_t bh = fdiv(rest, p.f_n_win);
+  t.win = int32_t(rest - bh * uint32_t(p.n_win));
+  t.bh = int32_t(bh);
   return t;
 }
 
@@ -585,8 +586,8 @@ __device__ __forceinline__ void win_attn_bf16_items(const Bf16KernelArgs& a) {
   }
 }
 
-// Plain shifted-window attention (§3.1), one item at a time: windows of one key tile or of
-// 16 and more, and tensors beyond the stream kernel's 32-bit offsets.
+// Plain shifted-window attention (§3.1), one item at a time: windows of one or two key tiles
+// or of more than 16, and tensors beyond the stream kernel's 32-bit offsets.
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void win_attn_bf16_kernel(
     Bf16KernelArgs a) {
@@ -605,8 +606,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 // The persistent workgroup walks items blockIdx.x, blockIdx.x + gridDim.x, ... as one
 // sequence of K/V tiles (global tile g = item sequence number * Tn + tile), so that the work
 // between two items is off the critical path:
-//   * the ring of K/V row offsets runs across items: the refill at step g writes tiles
-//     g+8 .. g+15, which near an item's end belong to the next item;
+//   * a ring of K/V row offsets holds two items: in the first step of an item every thread
+//     writes its share of the next item's row offsets (and query-row offsets), decoding
+//     that item once;
 //   * the K/V DMA of the last step of an item fetches the next item's first tile;
 //   * the next item's query-row offsets are computed in the first step of an item and its
 //     Q rows DMA'd into the Q buffer in the second (the Q buffer is free once an item's Q
@@ -615,9 +617,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 //     passes of 16 rows per wave (the other stage already holds the next item's first tile).
 // Every tensor is addressed through one buffer resource over the whole tensor, with byte
 // offsets bh * head_bytes + token * row_bytes: the launcher uses this kernel only when a
-// tensor fits in 0xffffff00 bytes and every window has at least two K/V tiles (one step
-// computes the next item's query rows, the next one loads them), and only for windows of
-// fewer than 16 key tiles, where the item transitions are a large share of the work.
+// tensor fits in 0xffffff00 bytes and every window has 3 to 16 K/V tiles (the ring holds
+// two items, and the next item's offsets, written in an item's first step, are read from
+// its second-to-last step on).
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void win_attn_bf16_stream_kernel(
     Bf16KernelArgs a) {
@@ -627,8 +629,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   constexpr int BN = C::BN, BM = C::BM, DK = C::DK, DB = C::DB;
   constexpr int RPG = L::RPG, RG = L::RG;
   constexpr int QG = LN::QG;
-  constexpr int TAB_TILES = 16;
-  constexpr int REFILL = 8;
+  constexpr int TAB_TILES = 32;  // ring slots: two items of at most 16 tiles
 
   __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char stage1[C::STAGE_BYTES];
@@ -654,30 +655,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // Q and out are touched a few times per item: their resources are built where used, from
   // the re-read arguments, so that they hold no scalar registers across the tile loop
 
-  // Byte offset (in the whole tensor) of row `local` of item `it`'s window; rows past the
-  // window get an offset beyond the resource range (zero reads, dropped writes).
-  auto item_row = [&](uint32_t it, int local) __attribute__((always_inline)) -> uint32_t {
-    const AttnParams& p = kernel_args().p;
-    const TileId tl = decode_tile(p, it, total);
-    const WinOrigin o = window_origin(p.map, uint32_t(tl.win));
-    return local < wtok ? uint32_t(tl.bh) * head_bytes + uint32_t(token_of(p.map, o, uint32_t(local))) * L::ROW_BYTES
-                        : 0xffffff00u;
-  };
-  auto item_qtile = [&](uint32_t it) __attribute__((always_inline)) -> int {
-    return decode_tile(kernel_args().p, it, total).qtile;
-  };
-
   // this workgroup's items: blockIdx.x + j * gridDim.x, j < n_items; global tiles g < g_end
   const uint32_t n_items = (total - blockIdx.x + gridDim.x - 1) / gridDim.x;
   const int g_end = int(n_items) * Tn;
   uint32_t item = blockIdx.x;  // current item
   int g0 = 0;                  // global index of its first tile
   int qb = 0;                  // which qrowtab holds its query-row offsets
-  // Offsets of the rows of ring tile g (global; g < g_end): tile g - j*Tn of item j = g / Tn.
-  auto fill_tile_rows = [&](int g, int row) __attribute__((always_inline)) {
-    const uint32_t j = fdiv(uint32_t(g), kernel_args().p.f_kv_tiles);
-    const int t = g - int(j) * Tn;
-    rowtab[(g % TAB_TILES) * BN + row] = item_row(blockIdx.x + j * gridDim.x, t * BN + row);
+  // All row offsets of item `it`, whose tiles are global tiles gfirst .. gfirst + Tn - 1:
+  // its key/value rows into their ring slots and its query rows into `qrow`, as byte offsets
+  // in the whole tensor (rows past the window get an offset beyond the resource range: zero
+  // reads, dropped writes). The item is decoded, and the parameters read, once for all.
+  auto fill_item = [&](uint32_t it, int gfirst, uint32_t* qrow) __attribute__((always_inline)) {
+    const AttnParams& p = kernel_args().p;
+    const TileId tl = decode_tile(p, it, total);
+    const WinOrigin o = window_origin(p.map, uint32_t(tl.win));
+    const uint32_t hb = uint32_t(tl.bh) * head_bytes;
+    auto row = [&](int local) __attribute__((always_inline)) -> uint32_t {
+      return local < wtok ? hb + uint32_t(token_of(p.map, o, uint32_t(local))) * L::ROW_BYTES : 0xffffff00u;
+    };
+    for (int e = tid; e < Tn * BN; e += C::NT) rowtab[((gfirst + e / BN) % TAB_TILES) * BN + e % BN] = row(e);
+    if (tid < BM) qrow[tid] = row(tl.qtile * BM + tid);
   };
   auto dma_tile = [&](const uint32_t* row_off, char* st) __attribute__((always_inline)) {
 #pragma unroll
@@ -703,14 +700,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                                  qrow[g * RPG + ln.ld_row] + ln.k_chunk_off);
   };
 
-  // ---- prologue: ring tiles 0 .. 15 and the first item's query rows
-  static_assert(BN == 64, "one ring tile per wave-wide fill");
-  for (int tt = wave; tt < TAB_TILES; tt += NW)
-    if (tt < g_end) fill_tile_rows(tt, lane);
-  {
-    const int qt = item_qtile(item);
-    if (tid < BM) qrowtab[0][tid] = item_row(item, qt * BM + tid);
-  }
+  // ---- prologue: the first item's key/value and query row offsets
+  fill_item(item, 0, qrowtab[0]);
   __syncthreads();
   uint32_t next_off[2 * C::LOADS];
   read_offs(0, next_off);
@@ -729,30 +720,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
   float m_run = -__builtin_inff(), l_run = 0.0f;
 
-  // Work of a few steps per item (the ring refill every REFILL steps; the next item's query
-  // rows in its first two steps): out of line, so that the common step runs straight through.
-  auto rare_work = [&](int g, int t) __attribute__((always_inline)) {
-    // refill the ring slots of tiles g-8 .. g-1 (all issued) with tiles g+8 .. g+15 that
-    // exist; first needed by the DMA of step g+7, published by this step's barrier
-    if (g % REFILL == 0 && g >= REFILL) {
-      for (int w = wave; w < REFILL; w += NW) {
-        const int gt = g + REFILL + w;
-        if (gt < g_end) fill_tile_rows(gt, lane);
-      }
-    }
-    if (g0 + Tn < g_end && t <= 1) {  // a next item exists
-      if (t == 0) {
-        // query-row offsets of the next item (its stores and its Q loads read them)
-        const uint32_t nx = item + gridDim.x;
-        const int qt = item_qtile(nx);
-        if (tid < BM) qrowtab[qb ^ 1][tid] = item_row(nx, qt * BM + tid);
-      } else {
-        // all of its Q rows in step 1 (measured 2-3 % faster on 4-tile items than spreading
-        // them over the item's steps: one short branch instead of a per-step range); a rolled
-        // loop keeps the DMA addresses out of the scalar registers held across the tile loop
+  // Work of the first two steps of an item that has a successor: out of line, so that the
+  // common step runs straight through.
+  auto rare_work = [&](int t) __attribute__((always_inline)) {
+    if (t == 0) {
+      // all row offsets of the next item, into the ring slots of its tiles (which held the
+      // previous item's, all read by now) and into the other query-row table. The ring
+      // holds two items, so these are first read in the step before the next item's first
+      // DMA, at least one barrier later (an item has at least 3 tiles).
+      fill_item(item + gridDim.x, g0 + Tn, qrowtab[qb ^ 1]);
+    } else {
+      // all of its Q rows in step 1 (measured 2-3 % faster on 4-tile items than spreading
+      // them over the item's steps: one short branch instead of a per-step range); a rolled
+      // loop keeps the DMA addresses out of the scalar registers held across the tile loop
 #pragma unroll 1
-        for (int i = 0; i < QG; ++i) dma_q(i, qrowtab[qb ^ 1]);
-      }
+      for (int i = 0; i < QG; ++i) dma_q(i, qrowtab[qb ^ 1]);
     }
   };
 
@@ -761,7 +743,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   auto step = [&](int g, const char* cur, char* nxt) __attribute__((always_inline)) -> bool {
     const int t = g - g0;
     if (__builtin_expect(g + 1 < g_end, 1)) dma_tile(next_off, nxt);
-    if (__builtin_expect((g % REFILL == 0 && g >= REFILL) || (g0 + Tn < g_end && t <= 1), 0)) rare_work(g, t);
+    if (__builtin_expect(g0 + Tn < g_end && t <= 1, 0)) rare_work(t);
     // Scalar loads the compiler issues above (parameters it re-reads instead of keeping them
     // in registers) return out of order with LDS reads; with one in flight, every wait for
     // the K fragments below would have to be a wait for all of them. Draining here lets the
@@ -1267,10 +1249,12 @@ static hipError_t launch_bf16(const void* q, const void* k, const void* v, void*
   using C = Bf16Cfg<D, NW>;
   p.q_tiles = (p.wtok + C::BM - 1) / C::BM;
   p.kv_tiles = (p.wtok + C::BN - 1) / C::BN;
-  p.f_kv_tiles = make_fastdiv(uint32_t(p.kv_tiles));
   p.mem_tiles = (p.n_mem + C::BN - 1) / C::BN;
   const uint64_t blocks = uint64_t(p.q_tiles) * uint64_t(p.n_win) * uint64_t(p.heads_total);
   if (blocks == 0 || blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
+  p.f_kv_tiles = make_fastdiv(uint32_t(p.kv_tiles));  // all three >= 1 here
+  p.f_q_tiles = make_fastdiv(uint32_t(p.q_tiles));
+  p.f_n_win = make_fastdiv(uint32_t(p.n_win));
   Bf16KernelArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -1282,17 +1266,18 @@ static hipError_t launch_bf16(const void* q, const void* k, const void* v, void*
   const hipError_t e = persistent_slots(&slots);
   if (e != hipSuccess) return e;
   const uint32_t grid = blocks < slots ? uint32_t(blocks) : slots;
-  // The stream kernel pays for its cross-item prefetch with a few scalar instructions and
-  // branches in every step; it is the faster one for windows of fewer than 16 key tiles
-  // (measured: FLUX-1024, 4 tiles, 4 % faster; 16 tiles and more, 1-3 % slower; dense 3-9 %
-  // slower). It addresses a whole tensor through one 32-bit buffer range (rows past a
-  // window at offsets from 0xffffff00 up), needs at least two K/V tiles per window and
-  // numbers a workgroup's tiles with 32-bit integers.
+  // The stream kernel takes the item transitions off the critical path (measured: FLUX-1024,
+  // 4 tiles, 8 % faster than the per-item kernel; FLUX-2048 and FLUX-4096, 16 tiles, 2-4 %
+  // faster). Its ring of row offsets holds two items of at most 16 tiles, the next item's
+  // offsets are written in an item's first step and read from its second-to-last step on
+  // (so at least 3 tiles), it addresses a whole tensor through one 32-bit buffer range
+  // (rows past a window at offsets from 0xffffff00 up) and numbers a workgroup's tiles with
+  // 32-bit integers.
   const uint64_t tensor_bytes = uint64_t(p.heads_total) * uint64_t(p.head_stride) * 2u;
   const uint64_t wg_tiles = (blocks + grid - 1) / grid * uint64_t(p.kv_tiles);
   if (p.route != nullptr || p.n_mem > 0 || p.lse != nullptr)
     hipLaunchKernelGGL((win_attn_bf16_ext_kernel<D, NW>), dim3(grid), dim3(C::NT), 0, stream, a);
-  else if (p.kv_tiles >= 2 && p.kv_tiles < 16 && tensor_bytes <= 0xffffff00u && wg_tiles < 0x7fffffffu)
+  else if (p.kv_tiles >= 3 && p.kv_tiles <= 16 && tensor_bytes <= 0xffffff00u && wg_tiles < 0x7fffffffu)
     hipLaunchKernelGGL((win_attn_bf16_stream_kernel<D, NW>), dim3(grid), dim3(C::NT), 0, stream, a);
   else
     hipLaunchKernelGGL((win_attn_bf16_kernel<D, NW>), dim3(grid), dim3(C::NT), 0, stream, a);
@@ -1308,6 +1293,8 @@ static hipError_t launch_f32(const void* q, const void* k, const void* v, void* 
   p.mem_tiles = (p.n_mem + C::BN - 1) / C::BN;
   const uint64_t blocks = uint64_t(p.q_tiles) * uint64_t(p.n_win) * uint64_t(p.heads_total);
   if (blocks == 0 || blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
+  p.f_q_tiles = make_fastdiv(uint32_t(p.q_tiles));  // both >= 1 here
+  p.f_n_win = make_fastdiv(uint32_t(p.n_win));
   hipLaunchKernelGGL((win_attn_f32_kernel<D>), dim3(uint32_t(blocks)), dim3(C::NT), 0, stream,
                      static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
                      static_cast<float*>(out), p);

@@ -17,6 +17,8 @@ struct AttnParams {
   int32_t q_tiles;      // filled by the launcher
   int32_t kv_tiles;     // filled by the launcher
   FastDiv f_kv_tiles;   // division by kv_tiles (stream kernel), filled by the launcher
+  FastDiv f_q_tiles;    // division by q_tiles (work-item decode), filled by the launcher
+  FastDiv f_n_win;      // division by n_win (work-item decode), filled by the launcher
   int32_t heads_total;  // B * heads
   int64_t head_stride;  // N * head_dim elements
   float scale_log2;     // log2(e) / sqrt(head_dim)

@@ -50,7 +50,7 @@ def kernel_name(dtype: str, window_tokens: int) -> str:
     if dtype != "bf16":
         return F32_KERNEL
     tiles = -(-window_tokens // 64)
-    return STREAM_KERNEL if 2 <= tiles < 16 else ATTN_KERNEL
+    return STREAM_KERNEL if 3 <= tiles <= 16 else ATTN_KERNEL
 
 
 def traffic_json_name(workload: str, tag: str = "") -> str:

@@ -31,9 +31,13 @@ CASES = [
     ("plain-d64-ragged", 1, 80, 64, (2, 20, 30), (2, 10, 15), (1, 4, -6), "plain", None, 302),
     ("memory-d128", 1, 100, 128, (1, 32, 32), (1, 8, 16), (0, 4, 8), "memory", (4, 4), 303),
     ("routed-memory-d64", 1, 100, 64, (1, 32, 32), (1, 8, 16), (0, 5, 3), "routed+memory", (4, 4), 304),
-    # windows of 8 and 15 key tiles (2 and 4 query tiles): the continuous-stream kernel
+    # windows of 3, 8, 15 and 16 key tiles: the continuous-stream kernel, whose ring of row
+    # offsets holds two items (3 and 16 tiles are its limits); 2 tiles: the per-item kernel
+    ("plain-d128-w192-3tiles", 1, 40, 128, (1, 48, 64), (1, 12, 16), (0, 5, 7), "plain", None, 307),
     ("plain-d128-w512", 1, 80, 128, (1, 32, 64), (1, 16, 32), (0, 5, 9), "plain", None, 305),
     ("plain-d128-w960-ragged", 1, 40, 128, (1, 48, 80), (1, 24, 40), (0, 7, -11), "plain", None, 306),
+    ("plain-d64-w1024-16tiles", 1, 24, 64, (1, 64, 128), (1, 32, 32), (0, 9, 21), "plain", None, 309),
+    ("plain-d64-w128-2tiles", 1, 72, 64, (1, 32, 32), (1, 8, 16), (0, 3, 9), "plain", None, 308),
 ]
 
 

@@ -28,7 +28,8 @@ def _counters(path, rows):
 
 
 def test_traffic_scaling(tmp_path):
-    k = "void basa::win_attn_bf16_kernel<128, 8>(...)"
+    wl = "flux-2048-128x128-w32"
+    k = f"void basa::{profiling.kernel_name('bf16', BY_NAME[wl].window_tokens)}<128, 8>(...)"
     c = "__amd_rocclr_copyBuffer"
     _counters(tmp_path / "f", [(k, "FETCH_SIZE", 100.0), (k, "FETCH_SIZE", 102.0), ("other", "FETCH_SIZE", 1e9)])
     _counters(tmp_path / "w", [(k, "WRITE_SIZE", 50.0)])
@@ -36,7 +37,6 @@ def test_traffic_scaling(tmp_path):
     _counters(tmp_path / "cf", [(c, "FETCH_SIZE", half)])                  # counter reads half the bytes
     _counters(tmp_path / "cw", [(c, "WRITE_SIZE", profiling.COPY_BYTES / 1024)])
     out = tmp_path / "out"
-    wl = "flux-2048-128x128-w32"
     profiling.main(["traffic", "--fetch", str(tmp_path / "f"), "--write", str(tmp_path / "w"),
                     "--copy-fetch", str(tmp_path / "cf"), "--copy-write", str(tmp_path / "cw"),
                     "--workload", wl, "--cmd", "cmd", "--out-dir", str(out)])
@@ -128,8 +128,9 @@ def test_bench_refuses_more_than_one_gpu():
 def test_counter_summary(tmp_path):
     """MFMA/VALU/LDS record: counters are averaged over the kernel's dispatches and related
     to the algorithmic MFMA count of the workload."""
-    k = "void basa::win_attn_bf16_kernel<128, 8>(...)"
     wl = BY_NAME["flux-2048-128x128-w32"]
+    kname = profiling.kernel_name("bf16", wl.window_tokens)
+    k = f"void basa::{kname}<128, 8>(...)"
     n_mfma = wl.window_flops() / (32 * 32 * 16 * 2)
     mfma = [(k, "MfmaUtil", 50.0), (k, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 1000.0), (k, "GRBM_GUI_ACTIVE", 16000.0),
             (k, "SQ_INSTS_VALU_MFMA_MOPS_BF16", wl.window_flops() / 512), (k, "SQ_INSTS_MFMA", n_mfma),
@@ -141,7 +142,7 @@ def test_counter_summary(tmp_path):
     out = tmp_path / "out"
     profiling.main(["counters", "--mfma", str(tmp_path / "m"), "--valu", str(tmp_path / "v"), "--workload", wl.name,
                     "--cmd", "c1", "--cmd", "c2", "--out-dir", str(out)])
-    rec = json.load(open(out / f"win_attn_bf16_kernel.{wl.name}.window.counters.json"))
+    rec = json.load(open(out / f"{kname}.{wl.name}.window.counters.json"))
     assert rec["mfma_flop_counted_over_algorithmic"] == 1.0
     assert rec["mfma_instructions_over_algorithmic"] == 1.0
     assert rec["mfma_util_pct"] == 50.0
@@ -150,7 +151,7 @@ def test_counter_summary(tmp_path):
     assert rec["lds_bank_conflict_over_lds_active"] == 0.25
     assert rec["valu_per_mfma"] == 4.0 and rec["trans_f32_per_mfma"] == 1.0 and rec["lds_instr_per_mfma"] == 0.5
     assert rec["kernel_hash"] == kernel_hash()
-    assert (out / f"win_attn_bf16_kernel.{wl.name}.window.counters.md").exists()
+    assert (out / f"{kname}.{wl.name}.window.counters.md").exists()
 
 
 def test_host_info_fields():
@@ -165,14 +166,17 @@ def test_host_info_fields():
 
 def test_kernel_choice_mirrors_the_launcher():
     """The profile summaries name the kernel the library launches for a workload: fp32 inputs
-    the fp32 kernel, bf16 windows of 2-15 key tiles of 64 the stream kernel, else the per-item
+    the fp32 kernel, bf16 windows of 3-16 key tiles of 64 the stream kernel, else the per-item
     kernel (the launcher's rule in attn_kernels.hip)."""
     assert profiling.kernel_name("f32", 64) == "win_attn_f32_kernel"
     assert profiling.kernel_name("bf16", 64) == "win_attn_bf16_kernel"
-    assert profiling.kernel_name("bf16", 65) == "win_attn_bf16_stream_kernel"
+    assert profiling.kernel_name("bf16", 128) == "win_attn_bf16_kernel"
+    assert profiling.kernel_name("bf16", 129) == "win_attn_bf16_stream_kernel"
     assert profiling.kernel_name("bf16", 256) == "win_attn_bf16_stream_kernel"
     assert profiling.kernel_name("bf16", 960) == "win_attn_bf16_stream_kernel"
-    assert profiling.kernel_name("bf16", 1024) == "win_attn_bf16_kernel"
+    assert profiling.kernel_name("bf16", 1024) == "win_attn_bf16_stream_kernel"
+    assert profiling.kernel_name("bf16", 1025) == "win_attn_bf16_kernel"
+    assert profiling.kernel_name("bf16", 2730) == "win_attn_bf16_kernel"
     assert profiling._matches("void basa::win_attn_bf16_stream_kernel<128, 8>(basa::Bf16KernelArgs)",
                               "win_attn_bf16_stream_kernel")
     assert not profiling._matches("void basa::win_attn_bf16_stream_kernel<128, 8>(basa::Bf16KernelArgs)",
