@@ -35,6 +35,9 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "attn_launch.hpp"
 #include "index_map.hpp"
@@ -380,10 +383,80 @@ struct Bf16Lane {
 // One work item: query tile tile.qtile of window tile.win of head tile.bh. EXT enables the
 // routed window and the pooled memory; without them the key/value stream is the window's
 // own tiles and the kernel needs fewer scalar registers.
-template <int D, int NW, bool EXT>
+// The single argument of the bf16 kernels: the kernel's argument segment is this struct,
+// so the loops can re-read the parameters from it by address.
+struct Bf16KernelArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* out;
+  AttnParams p;
+  uint32_t total;       // work items
+  // Per-item kernels: work units >= split_from are the halves of items split_from .. total-1
+  // (split_from == total: none); part holds their partial results (SplitPart layout, pair
+  // index item - split_from) and arrive one counter per split item, zero between launches.
+  uint32_t split_from;
+  void* part;
+  uint32_t* arrive;
+};
+
+// The kernel's parameters, re-read from the argument segment through a pointer the compiler
+// cannot see through: kept in scalar registers across the loops they would spill.
+__device__ __forceinline__ const Bf16KernelArgs& kernel_args() {
+  using ArgPtr = const __attribute__((address_space(4))) Bf16KernelArgs*;
+  ArgPtr ap = (ArgPtr)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(ap));
+  return *(const Bf16KernelArgs*)ap;
+}
+
+// Partial result of half an item (a split item, see win_attn_bf16_items): per wave and lane,
+// DB*4 float4 chunks of the unnormalised O accumulators, then (m, l, 0, 0); chunk c of lane
+// l at float4 index c*64 + l, so that each chunk is one contiguous wave-wide access.
+template <int D, int NW>
+struct SplitPart {
+  static constexpr int CHUNKS = D / 32 * 4 + 1;
+  static constexpr uint64_t HALF_BYTES = uint64_t(NW) * CHUNKS * 64 * 16;  // one half of one item
+};
+
+// LDS of one item of the per-item kernels, one set per <D, NW>, shared by the whole-item and
+// the half-item code (function-local __shared__ arrays: declared in the item function, each
+// instantiation would get its own). The two stages are separate objects: with the stage fixed
+// at compile time in each half of the unrolled tile loop, the compiler can tell that the
+// transpose reads of one stage do not alias the DMA into the other and does not make them
+// wait for it.
+template <int D, int NW>
+struct ItemLds {
+  using C = Bf16Cfg<D, NW>;
+  static constexpr int QBUF_BYTES = NW * (32 / TileLayout<D>::RPG) * TileLayout<D>::RG;
+  static constexpr int TAB_TILES = 16;  // ring of K/V row offsets, in tiles
+  __device__ static __forceinline__ char* stage0() {
+    __shared__ __attribute__((aligned(1024))) char b[C::STAGE_BYTES];
+    return b;
+  }
+  __device__ static __forceinline__ char* stage1() {
+    __shared__ __attribute__((aligned(1024))) char b[C::STAGE_BYTES];
+    return b;
+  }
+  __device__ static __forceinline__ char* qbuf() {
+    __shared__ __attribute__((aligned(1024))) char b[QBUF_BYTES];
+    return b;
+  }
+  __device__ static __forceinline__ uint32_t* rowtab() {
+    __shared__ uint32_t b[TAB_TILES * C::BN];
+    return b;
+  }
+  __device__ static __forceinline__ uint32_t* qrowtab() {
+    __shared__ uint32_t b[C::BM];
+    return b;
+  }
+};
+
+// HALF: the work item is one half of a split item (key tiles [0, Th) for half 0, [Th, Tn) for
+// half 1, Th = ceil(Tn / 2)); the two halves are merged by whichever finishes second.
+template <int D, int NW, bool EXT, bool HALF>
 __device__ __forceinline__ void win_attn_bf16_item(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                    const uint16_t* __restrict__ v, uint16_t* __restrict__ out,
-                                                   const AttnParams& p, uint32_t item, uint32_t total) {
+                                                   const AttnParams& p, uint32_t item, uint32_t total, int half) {
   using C = Bf16Cfg<D, NW>;
   using L = TileLayout<D>;
   using LN = Bf16Lane<D, NW>;
@@ -391,11 +464,9 @@ __device__ __forceinline__ void win_attn_bf16_item(const uint16_t* __restrict__ 
   constexpr int RPG = L::RPG, RG = L::RG;
   constexpr int QG = LN::QG;
 
-  // Two stages as separate objects: with the stage fixed at compile time in each half of
-  // the unrolled tile loop, the compiler can tell that the transpose reads of one stage do
-  // not alias the DMA into the other and does not make them wait for it.
-  __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char stage1[C::STAGE_BYTES];
+  using LDS = ItemLds<D, NW>;
+  char* const stage0 = LDS::stage0();
+  char* const stage1 = LDS::stage1();
 
   // threadIdx.x through an opaque move: in the item loop of the persistent kernel the
   // compiler would otherwise hoist the lane-derived values of the prologue and keep them
@@ -424,6 +495,10 @@ __device__ __forceinline__ void win_attn_bf16_item(const uint16_t* __restrict__ 
   const int Tw = p.kv_tiles;
   const int Tr = routed < 0 ? 0 : Tw;
   const int Tn = EXT ? Tw + Tr + p.mem_tiles : Tw;
+  // key tiles [t0, t1) of the stream; the whole stream unless HALF
+  const int Th = (Tn + 1) >> 1;
+  const int t0 = HALF && half == 1 ? Th : 0;
+  const int t1 = HALF && half == 0 ? Th : Tn;
   const int64_t mem_base = int64_t(tile.bh) * int64_t(p.n_mem) * D;
   const uint32_t mem_bytes = uint32_t(p.n_mem) * uint32_t(L::ROW_BYTES);
   const __amdgpu_buffer_rsrc_t kmrs = make_rsrc(static_cast<const uint16_t*>(p.kmem) + mem_base, mem_bytes);
@@ -462,9 +537,9 @@ __device__ __forceinline__ void win_attn_bf16_item(const uint16_t* __restrict__ 
   // ring of TAB_TILES tiles in LDS (one row per thread per refill), and each lane reads the
   // LOADS offsets it needs one step before it issues the DMA. The shift/partition index
   // arithmetic thus costs a few instructions per 8 tiles instead of several per row.
-  constexpr int TAB_TILES = 16;
+  constexpr int TAB_TILES = LDS::TAB_TILES;
   constexpr int REFILL = 8;  // tiles per refill
-  __shared__ uint32_t rowtab[TAB_TILES * BN];
+  uint32_t* const rowtab = LDS::rowtab();
   auto fill_tab = [&](int first, int ntiles) __attribute__((always_inline)) {
     for (int e = tid; e < ntiles * BN; e += C::NT) {
       const int t = first + e / BN;
@@ -482,23 +557,24 @@ __device__ __forceinline__ void win_attn_bf16_item(const uint16_t* __restrict__ 
     }
   };
 
-  {  // tile 0 straight from the index map, the table for tiles 0 .. TAB_TILES - 1
+  {  // tile t0 straight from the index map, the table for tiles t0 .. t0 + TAB_TILES - 1
     uint32_t off0[2 * C::LOADS];
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-      off0[i] = row_offset((wave * C::LOADS + i) * RPG + ln.ld_row);
-      off0[C::LOADS + i] = row_offset((wave * C::LOADS + i) * RPG + ln.v_ld_row);
+      off0[i] = tile_row_offset(t0, (wave * C::LOADS + i) * RPG + ln.ld_row);
+      off0[C::LOADS + i] = tile_row_offset(t0, (wave * C::LOADS + i) * RPG + ln.v_ld_row);
     }
-    dma_tile(off0, stage0, 0);
+    dma_tile(off0, stage0, t0);
   }
-  fill_tab(0, min(TAB_TILES, Tn));
+  fill_tab(t0, min(TAB_TILES, t1 - t0));
 
   // ---- Q: each wave DMAs its own 32 rows into the Q buffer (laid out like a K tile, 4 whole
   // rows per wave-wide load), and after the prologue barrier reads its fragments from there.
   // Q is read once per workgroup: non-temporal loads keep it out of the way of the K/V in L2.
   // qrowtab keeps the byte offset of every query row for the output stores.
-  __shared__ __attribute__((aligned(1024))) char qbuf[NW * QG * RG];
-  __shared__ uint32_t qrowtab[BM];
+  static_assert(LDS::QBUF_BYTES == NW * QG * RG, "Q buffer size");
+  char* const qbuf = LDS::qbuf();
+  uint32_t* const qrowtab = LDS::qrowtab();
   {
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q + base, head_bytes);
 #pragma unroll
@@ -521,11 +597,12 @@ __device__ __forceinline__ void win_attn_bf16_item(const uint16_t* __restrict__ 
   // holds the row offsets of tile t+1 (read from the table during the previous step).
   uint32_t next_off[2 * C::LOADS];
   auto tile_step = [&](int t, const char* cur, char* nxt) {
-    if (t + 1 < Tn) dma_tile(next_off, nxt, t + 1);
-    if (t + 2 < Tn) read_offs(t + 2, next_off);
+    if (t + 1 < t1) dma_tile(next_off, nxt, t + 1);
+    if (t + 2 < t1) read_offs(t + 2, next_off);
     // refill the ring slots of tiles t-8 .. t-1 (all issued) with tiles t+8 .. t+15, first
     // needed by the DMA of step t+7; the barrier ending this step publishes them
-    if (t % REFILL == 0 && t >= REFILL && t + REFILL < Tn) fill_tab(t + REFILL, min(REFILL, Tn - t - REFILL));
+    if ((t - t0) % REFILL == 0 && t - t0 >= REFILL && t + REFILL < t1)
+      fill_tab(t + REFILL, min(REFILL, t1 - t - REFILL));
     // ragged last tile of the window, the routed window or the memory
     const int lim = !EXT || t < Tw ? p.wtok - t * BN : t < Tw + Tr ? p.wtok - (t - Tw) * BN : p.n_mem - (t - Tw - Tr) * BN;
     f32x16_t sacc[2];
@@ -536,12 +613,61 @@ __device__ __forceinline__ void win_attn_bf16_item(const uint16_t* __restrict__ 
     __syncthreads();  // next tile resident; everyone is done with this stage
   };
 
-  __syncthreads();  // tile 0 and Q resident, row tables written
+  __syncthreads();  // tile t0 and Q resident, row tables written
   ln.load_q(qbuf, qf);
-  if (1 < Tn) read_offs(1, next_off);
-  for (int t = 0; t < Tn; t += 2) {
+  if (t0 + 1 < t1) read_offs(t0 + 1, next_off);
+  for (int t = t0; t < t1; t += 2) {
     tile_step(t, stage0, stage1);
-    if (t + 1 < Tn) tile_step(t + 1, stage1, stage0);
+    if (t + 1 < t1) tile_step(t + 1, stage1, stage0);
+  }
+
+  if constexpr (HALF) {
+    // Both halves write their partial (O, m, l); the one that arrives second at the item's
+    // counter reads the other's and finishes the item. Every wave's stores are complete at
+    // the barrier, and the counter's agent-scope release and acquire make them visible to
+    // the other half on another XCD.
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    using SP = SplitPart<D, NW>;
+    const Bf16KernelArgs& a = kernel_args();
+    const uint32_t pair = item - a.split_from;
+    f32x4_t* part = reinterpret_cast<f32x4_t*>(a.part);
+    f32x4_t* mine = part + ((uint64_t(pair) * 2 + uint64_t(half)) * NW + uint64_t(wave)) * (SP::CHUNKS * 64) + lane;
+    const f32x4_t* other = part + ((uint64_t(pair) * 2 + uint64_t(half ^ 1)) * NW + uint64_t(wave)) * (SP::CHUNKS * 64) + lane;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        mine[(db * 4 + j) * 64] = f32x4_t{oacc[db][4 * j], oacc[db][4 * j + 1], oacc[db][4 * j + 2], oacc[db][4 * j + 3]};
+    mine[DB * 4 * 64] = f32x4_t{m_run, l_run, 0.0f, 0.0f};
+    __shared__ uint32_t first;
+    __syncthreads();
+    if (tid == 0)
+      first = __hip_atomic_fetch_add(a.arrive + pair, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == 0u;
+    __syncthreads();
+    if (first) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    // O = O0 2^(m0 - m) + O1 2^(m1 - m), l likewise, m = max(m0, m1), with half 0's terms
+    // always first: the result does not depend on which half merges.
+    const f32x4_t ml = other[DB * 4 * 64];
+    const float m0 = half == 0 ? m_run : ml[0], m1 = half == 0 ? ml[0] : m_run;
+    const float l0 = half == 0 ? l_run : ml[1], l1 = half == 0 ? ml[1] : l_run;
+    const float mx = fmaxf(m0, m1);
+    const float s0 = __builtin_amdgcn_exp2f(m0 - mx), s1 = __builtin_amdgcn_exp2f(m1 - mx);
+    m_run = mx;
+    l_run = l0 * s0 + l1 * s1;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4_t o = other[(db * 4 + j) * 64];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float own = oacc[db][4 * j + e];
+          oacc[db][4 * j + e] = (half == 0 ? own : o[e]) * s0 + (half == 0 ? o[e] : own) * s1;
+        }
+      }
+    // the counter starts the next launch at zero
+    if (tid == 0) __hip_atomic_store(a.arrive + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // ---- normalise and store each row at its original (un-shifted) position, staged through
@@ -555,33 +681,23 @@ __device__ __forceinline__ void win_attn_bf16_item(const uint16_t* __restrict__ 
   }
 }
 
-// The single argument of the kernels below: the kernel's argument segment is this struct,
-// so the loops can re-read the parameters from it by address.
-struct Bf16KernelArgs {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
-  uint16_t* out;
-  AttnParams p;
-  uint32_t total;  // work items
-};
-
-// The kernel's parameters, re-read from the argument segment through a pointer the compiler
-// cannot see through: kept in scalar registers across the loops they would spill.
-__device__ __forceinline__ const Bf16KernelArgs& kernel_args() {
-  using ArgPtr = const __attribute__((address_space(4))) Bf16KernelArgs*;
-  ArgPtr ap = (ArgPtr)__builtin_amdgcn_kernarg_segment_ptr();
-  asm volatile("" : "+s"(ap));
-  return *(const Bf16KernelArgs*)ap;
-}
-
-// Per-item kernels: a persistent grid of (at most) one workgroup per CU walks the work items
+// Per-item kernels: a persistent grid of (at most) one workgroup per CU walks the work units
 // blockIdx.x, blockIdx.x + gridDim.x, ... This drops the CU's gap between workgroups, which
-// is a visible share of a 16-tile item.
+// is a visible share of a 16-tile item. When the last round would leave more than half of the
+// grid idle, its items are split in two along the key stream (unit split_from + 2j + h is half
+// h of item split_from + j), so that it takes about half an item instead of a whole one.
 template <int D, int NW, bool EXT>
 __device__ __forceinline__ void win_attn_bf16_items(const Bf16KernelArgs& a) {
-  for (uint32_t item = blockIdx.x; item < a.total; item += gridDim.x) {
-    win_attn_bf16_item<D, NW, EXT>(a.q, a.k, a.v, a.out, kernel_args().p, item, a.total);
+  const uint32_t split_from = a.split_from;
+  const uint32_t units = split_from + 2 * (a.total - split_from);
+  for (uint32_t u = blockIdx.x; u < units; u += gridDim.x) {
+    if (u < split_from) {
+      win_attn_bf16_item<D, NW, EXT, false>(a.q, a.k, a.v, a.out, kernel_args().p, u, a.total, 0);
+    } else {
+      const uint32_t s = u - split_from;
+      win_attn_bf16_item<D, NW, EXT, true>(a.q, a.k, a.v, a.out, kernel_args().p, split_from + (s >> 1), a.total,
+                                           int(s & 1u));
+    }
     __syncthreads();  // the next item's prologue rewrites LDS the epilogue may still read
   }
 }
@@ -1243,6 +1359,48 @@ static hipError_t persistent_slots(uint32_t* slots) {
   return hipSuccess;
 }
 
+// Workspace of split items for the per-item kernels: for each of at most slots/2 items, two
+// SplitPart halves (sized for D = 128, which also holds D = 64), then one arrival counter per
+// item. The counters are zeroed when the workspace is made and every launch leaves them at
+// zero (the merging half resets its item's).
+static uint64_t split_counter_offset(uint32_t slots) {
+  return uint64_t(slots / 2) * 2 * SplitPart<128, 8>::HALF_BYTES;
+}
+static uint64_t split_workspace_bytes(uint32_t slots) {
+  return split_counter_offset(slots) + uint64_t(slots / 2) * 4;
+}
+
+// The library's own workspace, one per (device, stream), made on the first launch on that
+// stream that splits items and kept until the process ends. Launches on one stream run in
+// order, so they can share it; launches on different streams never do. Returns null (no
+// split) while the stream is being captured into a graph and has no workspace yet, or when
+// the allocation fails.
+static void* split_workspace(hipStream_t stream, uint32_t slots) {
+  static std::mutex mu;
+  static std::map<std::pair<int, hipStream_t>, void*> made;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(dev, stream);
+  const auto it = made.find(key);
+  if (it != made.end()) return it->second;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return nullptr;
+  void* ws = nullptr;
+  if (hipMalloc(&ws, split_workspace_bytes(slots)) != hipSuccess) {
+    (void)hipGetLastError();  // not an error of this launch: it runs unsplit
+    return nullptr;
+  }
+  if (hipMemsetAsync(static_cast<char*>(ws) + split_counter_offset(slots), 0, uint64_t(slots / 2) * 4, stream) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipFree(ws);
+    return nullptr;
+  }
+  made.emplace(key, ws);
+  return ws;
+}
+
 template <int D, int NW>
 static hipError_t launch_bf16(const void* q, const void* k, const void* v, void* out, AttnParams p,
                               hipStream_t stream) {
@@ -1262,6 +1420,9 @@ static hipError_t launch_bf16(const void* q, const void* k, const void* v, void*
   a.out = static_cast<uint16_t*>(out);
   a.p = p;
   a.total = uint32_t(blocks);
+  a.split_from = a.total;
+  a.part = nullptr;
+  a.arrive = nullptr;
   uint32_t slots = 0;
   const hipError_t e = persistent_slots(&slots);
   if (e != hipSuccess) return e;
@@ -1275,9 +1436,24 @@ static hipError_t launch_bf16(const void* q, const void* k, const void* v, void*
   // 32-bit integers.
   const uint64_t tensor_bytes = uint64_t(p.heads_total) * uint64_t(p.head_stride) * 2u;
   const uint64_t wg_tiles = (blocks + grid - 1) / grid * uint64_t(p.kv_tiles);
-  if (p.route != nullptr || p.n_mem > 0 || p.lse != nullptr)
+  const bool ext = p.route != nullptr || p.n_mem > 0 || p.lse != nullptr;
+  const bool stream_kernel =
+      !ext && p.kv_tiles >= 3 && p.kv_tiles <= 16 && tensor_bytes <= 0xffffff00u && wg_tiles < 0x7fffffffu;
+  // Per-item kernels: split the items of a last round that would fill at most half the grid
+  // (each half needs a key tile of its own). Measured on the 21x30x52 Wan grid (3168 items of
+  // 43 tiles on 256 CUs, 96 in the last round): 2.5-4 % faster.
+  const uint32_t tail = uint32_t(blocks % grid);
+  if (!stream_kernel && blocks > grid && tail != 0 && tail <= grid / 2 && p.kv_tiles >= 2) {
+    void* ws = split_workspace(stream, slots);
+    if (ws != nullptr) {
+      a.split_from = uint32_t(blocks) - tail;
+      a.part = ws;
+      a.arrive = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + split_counter_offset(slots));
+    }
+  }
+  if (ext)
     hipLaunchKernelGGL((win_attn_bf16_ext_kernel<D, NW>), dim3(grid), dim3(C::NT), 0, stream, a);
-  else if (p.kv_tiles >= 3 && p.kv_tiles <= 16 && tensor_bytes <= 0xffffff00u && wg_tiles < 0x7fffffffu)
+  else if (stream_kernel)
     hipLaunchKernelGGL((win_attn_bf16_stream_kernel<D, NW>), dim3(grid), dim3(C::NT), 0, stream, a);
   else
     hipLaunchKernelGGL((win_attn_bf16_kernel<D, NW>), dim3(grid), dim3(C::NT), 0, stream, a);

@@ -7,8 +7,10 @@ several hundred items, so that most workgroups run two to four, in uneven number
 output element (and the log-sum-exp where written) is compared with the fp64 reference:
 plain windows (both head dims, a ragged window), pooled memory, and a routed window with
 memory. A second set has item counts just below, at and just above the CU count and twice
-it (255, 256, 257, 513). Bars as everywhere: bf16 rel-L2 <= 5e-3 and max-abs <= 2e-2, LSE
-max-abs <= 3e-3.
+it (255, 256, 257, 513). A third set runs the per-item kernel with a last round of at most
+half the grid, whose items are split in two along the key stream and merged by the half
+that finishes second (the memory and 2-tile cases above are split as well). Bars as
+everywhere: bf16 rel-L2 <= 5e-3 and max-abs <= 2e-2, LSE max-abs <= 3e-3.
 """
 import math
 
@@ -54,6 +56,42 @@ EDGE = [
     ("257-items", 257, 64, (1, 8, 8), (1, 8, 8), (0, 1, 1), 313),
     ("513-items", 19, 128, (3, 24, 24), (1, 8, 8), (1, 3, 5), 314),
 ]
+
+
+# per-item kernel (windows of more than 16 key tiles), 256 < items <= 384: the last round is
+# split. Ragged 17-tile windows (1080 keys), so the halves are 9 and 8 tiles and the second
+# half ends in a partial tile. name, heads, head_dim, grid, window, shift, seed
+SPLIT = [
+    ("split-d128-w1080", 19, 128, (1, 48, 90), (1, 24, 45), (0, 7, -11), 321),
+    ("split-d64-w1080", 18, 64, (1, 48, 90), (1, 24, 45), (0, -5, 13), 322),
+]
+
+
+def test_split_cases_have_a_short_last_round():
+    for name, heads, d, grid, window, *_ in SPLIT:
+        n = work_items(1, heads, grid, window)
+        assert CUS < n <= CUS + CUS // 2, (name, n)
+        assert math.ceil(int(np.prod(window)) / 64) > 16, name
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", SPLIT, ids=[c[0] for c in SPLIT])
+def test_split_items_every_element(case):
+    name, heads, d, grid, window, shift, seed = case
+    N = int(np.prod(grid))
+    t = inputs.draw_qkv((1, heads, N, d), "bf16", seed)
+    dev = to_device(t)
+    log_case(name, "items", work_items(1, heads, grid, window), "grid", grid, "window", window, "shift", shift)
+    outs = []
+    for _ in range(2):
+        out = torch.full_like(dev["q"], float("nan"))
+        _lib.window_attn_fwd(dev["q"], dev["k"], dev["v"], out, grid, window, shift)
+        torch.cuda.synchronize()
+        outs.append(out)
+    # the merged halves are added in a fixed order: the same result whichever half merges
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), name
+    ref = O.window_attention(t.f64("q"), t.f64("k"), t.f64("v"), grid, window, shift)
+    assert_parity(to_host(outs[0]), ref, "bf16", name)
 
 
 def test_edge_item_counts():
