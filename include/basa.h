@@ -17,13 +17,28 @@
  *   - Tensors are contiguous [B, heads, N, head_dim], N = T*H*W tokens flattened
  *     row-major over (t, h, w). q, k, v, out hold the same element type.
  *   - All tensor pointers are DEVICE pointers owned by the caller and must be 16-byte
- *     aligned. The library allocates nothing. Its only state is the compute-unit count of
- *     each device, read on the first bf16 call there and cached (thread-safe).
+ *     aligned. The library's own state is the compute-unit count of each device, read on
+ *     the first bf16 call there and cached (thread-safe), and the workspaces of split work
+ *     items (next item).
+ *   - Split work items (bf16 only). The kernel that walks one work item at a time (windows
+ *     of 2 or more than 16 key tiles of 64 tokens, the dense baseline, pooled memory,
+ *     routed windows, log-sum-exp) splits the items of a last round that would occupy at
+ *     most half of the compute units into two halves along the key stream; the half that
+ *     finishes second merges them. The halves' partial results go to a workspace of one
+ *     (device, stream): for 256 compute units 35.7 MB (128 items x 2 halves x 139,264
+ *     bytes, and 4 bytes per item), allocated with hipMalloc, its counters cleared with
+ *     hipMemsetAsync on `stream`, on the first call on that stream that splits, and kept
+ *     until the process ends. Calls on one stream share it (they run in order); calls on
+ *     different streams never do. A stream destroyed while such a call on it still runs
+ *     must not be followed, before that call ends, by a new stream with the same handle.
+ *     If the allocation fails, or the stream is being captured into a graph and has no
+ *     workspace yet, the call runs unsplit (the same result within the bf16 bounds).
  *   - Calls are asynchronous on `stream` (0 = the null stream) and return once the work
- *     is enqueued. They allocate, clear and synchronise nothing, so a sequence of calls can
- *     be captured in a HIP graph and replayed (after a first call on the device, outside
- *     the capture, has read its compute-unit count). Argument errors are reported before any HIP call is made; no entry
- *     point aborts, throws or prints.
+ *     is enqueued. Apart from a stream's first split call (above) they allocate, clear and
+ *     synchronise nothing, so a sequence of calls can be captured in a HIP graph and
+ *     replayed (after a first call on the device, outside the capture, has read its
+ *     compute-unit count). Argument errors are reported before any HIP call is made; no
+ *     entry point aborts, throws or prints.
  *   - The softmax scale is 1/sqrt(head_dim); softmax statistics are kept in fp32.
  *   - Supported: dtype BASA_DTYPE_F32 or BASA_DTYPE_BF16, head_dim 64 or 128.
  */
