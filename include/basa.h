@@ -67,7 +67,10 @@ typedef enum {
                                T*H*W, B*heads and N*head_dim must not exceed 2^31-1, and
                                for bf16 one head must not exceed 0xffffff00 bytes */
   BASA_ERR_HIP = 6,         /* the HIP runtime rejected the launch (hipGetLastError) */
-  BASA_ERR_ALIGN = 7        /* a tensor pointer is not 16-byte aligned */
+  BASA_ERR_ALIGN = 7,       /* a tensor pointer is not 16-byte aligned */
+  BASA_ERR_SCRATCH = 8      /* basa_window_attn_fwd_noalloc: the split work items need more
+                               than the static scratch buffer holds (grids of more than 256
+                               workgroups; never on MI355X) */
 } basa_status;
 
 /*
@@ -89,6 +92,21 @@ int basa_window_attn_fwd(const void* q, const void* k, const void* v, void* out,
                          int B, int heads, int T, int H, int W,
                          int wt, int wh, int ww, int st, int sh, int sw,
                          int head_dim, int dtype, hipStream_t stream);
+
+/*
+ * basa_window_attn_fwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid it. Same arguments, result and errors,
+ * plus BASA_ERR_SCRATCH. It calls no hipMalloc, hipFree or other allocating routine: split
+ * work items keep their partial results in a static device array of the library (35.7 MB per
+ * device, held until the process ends; room for 128 split items, i.e. grids of up to 256
+ * workgroups). Its counters are cleared by a small kernel on `stream` at every call that
+ * splits (no memset). Every call on a device uses the same array, so calls that overlap on
+ * one device (different streams, or host threads) race; calls in order on one stream do not.
+ */
+int basa_window_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out,
+                                 int B, int heads, int T, int H, int W,
+                                 int wt, int wh, int ww, int st, int sh, int sw,
+                                 int head_dim, int dtype, hipStream_t stream);
 
 /*
  * Dense softmax attention over all N tokens: the baseline the paper's speedups are

@@ -18,7 +18,7 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 
 # Exported C symbols, in header order.
-SYMBOLS = ("basa_window_attn_fwd", "basa_full_attn_fwd", "basa_pool_kv", "basa_window_attn_mem_fwd",
+SYMBOLS = ("basa_window_attn_fwd", "basa_window_attn_fwd_noalloc", "basa_full_attn_fwd", "basa_pool_kv", "basa_window_attn_mem_fwd",
            "basa_window_means", "basa_route_top1", "basa_window_attn_routed_fwd", "basa_window_perm",
            "basa_shift_schedule", "basa_status_string", "basa_version")
 
@@ -43,6 +43,8 @@ def load() -> ctypes.CDLL:
     vp, i = ctypes.c_void_p, ctypes.c_int
     lib.basa_window_attn_fwd.argtypes = [vp, vp, vp, vp] + [i] * 13 + [vp]
     lib.basa_window_attn_fwd.restype = i
+    lib.basa_window_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp] + [i] * 13 + [vp]
+    lib.basa_window_attn_fwd_noalloc.restype = i
     lib.basa_full_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.basa_full_attn_fwd.restype = i
     lib.basa_pool_kv.argtypes = [vp, vp, vp, vp] + [i] * 9 + [vp]
@@ -127,6 +129,21 @@ def window_attn_fwd(q, k, v, out, grid, window, shift, stream=None) -> None:
                                      wt, wh, ww, st, sh, sw, d, _dtype_code(q), _stream_handle(stream))
     if rc != 0:
         raise BasaError(rc, "basa_window_attn_fwd")
+
+
+def window_attn_fwd_noalloc(q, k, v, out, grid, window, shift, stream=None) -> None:
+    """``window_attn_fwd`` through the entry point that allocates nothing (static scratch)."""
+    _check_tensors(q, k, v, out)
+    B, H_, N, d = q.shape
+    T, H, W = (int(x) for x in grid)
+    wt, wh, ww = (int(x) for x in window)
+    st, sh, sw = (int(x) for x in shift)
+    if T * H * W != N:
+        raise BasaError(2, f"grid {grid} holds {T * H * W} tokens, tensors hold {N}")
+    rc = load().basa_window_attn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H_, T, H,
+                                             W, wt, wh, ww, st, sh, sw, d, _dtype_code(q), _stream_handle(stream))
+    if rc != 0:
+        raise BasaError(rc, "basa_window_attn_fwd_noalloc")
 
 
 def full_attn_fwd(q, k, v, out, stream=None) -> None:

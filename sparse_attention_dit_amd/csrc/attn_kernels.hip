@@ -1363,11 +1363,46 @@ static hipError_t persistent_slots(uint32_t* slots) {
 // SplitPart halves (sized for D = 128, which also holds D = 64), then one arrival counter per
 // item. The counters are zeroed when the workspace is made and every launch leaves them at
 // zero (the merging half resets its item's).
-static uint64_t split_counter_offset(uint32_t slots) {
+static constexpr uint64_t split_counter_offset(uint32_t slots) {
   return uint64_t(slots / 2) * 2 * SplitPart<128, 8>::HALF_BYTES;
 }
-static uint64_t split_workspace_bytes(uint32_t slots) {
+static constexpr uint64_t split_workspace_bytes(uint32_t slots) {
   return split_counter_offset(slots) + uint64_t(slots / 2) * 4;
+}
+
+// The workspace of basa_window_attn_fwd_noalloc, for callers that cannot allocate: a static
+// device array (one per device the library runs on, held until the process ends) in the
+// split-workspace layout for grids of up to kScratchSlots workgroups, i.e. at most 128 split
+// items: 35.7 MB. Every such call on a device uses the same array; calls that overlap on one
+// device race. Host code uses the address from scratch_address(), never the array's name
+// (which on the host is a stand-in, not a device address).
+constexpr uint32_t kScratchSlots = 256;
+static __device__ __attribute__((aligned(256))) char scratch[split_workspace_bytes(kScratchSlots)];
+
+// Device address of `scratch` on the current device, looked up once per device.
+static hipError_t scratch_address(void** addr) {
+  static std::mutex mu;
+  static void* known[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (known[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    known[dev] = p;
+  }
+  *addr = known[dev];
+  return hipSuccess;
+}
+
+// Zero n counters (a kernel rather than a memset, so that a graph capturing the call replays
+// it correctly).
+__global__ __launch_bounds__(256) void clear_counters_kernel(uint32_t* c, uint32_t n) {
+  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+  if (i < n) c[i] = 0u;
 }
 
 // The library's own workspace, one per (device, stream), made on the first launch on that
@@ -1401,9 +1436,11 @@ static void* split_workspace(hipStream_t stream, uint32_t slots) {
   return ws;
 }
 
+// no_alloc: split items keep their partial results in `scratch` instead of a workspace of the
+// stream (hipErrorOutOfMemory if the split needs more than it holds).
 template <int D, int NW>
 static hipError_t launch_bf16(const void* q, const void* k, const void* v, void* out, AttnParams p,
-                              hipStream_t stream) {
+                              bool no_alloc, hipStream_t stream) {
   using C = Bf16Cfg<D, NW>;
   p.q_tiles = (p.wtok + C::BM - 1) / C::BM;
   p.kv_tiles = (p.wtok + C::BN - 1) / C::BN;
@@ -1444,11 +1481,24 @@ static hipError_t launch_bf16(const void* q, const void* k, const void* v, void*
   // 43 tiles on 256 CUs, 96 in the last round): 2.5-4 % faster.
   const uint32_t tail = uint32_t(blocks % grid);
   if (!stream_kernel && blocks > grid && tail != 0 && tail <= grid / 2 && p.kv_tiles >= 2) {
-    void* ws = split_workspace(stream, slots);
+    void* ws = nullptr;
+    uint64_t counters = 0;
+    if (no_alloc) {
+      if (tail > kScratchSlots / 2) return hipErrorOutOfMemory;
+      const hipError_t es = scratch_address(&ws);
+      if (es != hipSuccess) return es;
+      counters = split_counter_offset(kScratchSlots);
+      // the array keeps the last call's contents: the counters of this call start at zero
+      hipLaunchKernelGGL(clear_counters_kernel, dim3((tail + 255) / 256), dim3(256), 0, stream,
+                         reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + counters), tail);
+    } else {
+      ws = split_workspace(stream, slots);
+      counters = split_counter_offset(slots);
+    }
     if (ws != nullptr) {
       a.split_from = uint32_t(blocks) - tail;
       a.part = ws;
-      a.arrive = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + split_counter_offset(slots));
+      a.arrive = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + counters);
     }
   }
   if (ext)
@@ -1478,10 +1528,10 @@ static hipError_t launch_f32(const void* q, const void* k, const void* v, void* 
 }
 
 hipError_t launch_window_attention(const void* q, const void* k, const void* v, void* out, const AttnParams& p,
-                                   int head_dim, bool bf16, hipStream_t stream) {
+                                   int head_dim, bool bf16, bool no_alloc, hipStream_t stream) {
   if (bf16) {
-    if (head_dim == 128) return launch_bf16<128, 8>(q, k, v, out, p, stream);
-    if (head_dim == 64) return launch_bf16<64, 8>(q, k, v, out, p, stream);
+    if (head_dim == 128) return launch_bf16<128, 8>(q, k, v, out, p, no_alloc, stream);
+    if (head_dim == 64) return launch_bf16<64, 8>(q, k, v, out, p, no_alloc, stream);
   } else {
     if (head_dim == 128) return launch_f32<128>(q, k, v, out, p, stream);
     if (head_dim == 64) return launch_f32<64>(q, k, v, out, p, stream);

@@ -35,8 +35,11 @@ struct AttnParams {
   const int32_t* route;
 };
 
+// no_alloc: the split work items of the bf16 per-item kernels use the library's static scratch
+// array instead of a workspace allocated for the stream (hipErrorOutOfMemory when the split
+// needs more than the array holds).
 hipError_t launch_window_attention(const void* q, const void* k, const void* v, void* out, const AttnParams& p,
-                                   int head_dim, bool bf16, hipStream_t stream);
+                                   int head_dim, bool bf16, bool no_alloc, hipStream_t stream);
 
 hipError_t launch_window_perm(const WinMap& map, int32_t wtok, int32_t total, int32_t* perm, hipStream_t stream);
 

@@ -43,7 +43,8 @@ int check_grid(int T, int H, int W, int wt, int wh, int ww) {
 // null lse, null route.
 int run_attention(const void* q, const void* k, const void* v, const int32_t* route, const void* kmem,
                   const void* vmem, int n_mem, void* out, float* lse, int B, int heads, int T, int H, int W, int wt,
-                  int wh, int ww, int st, int sh, int sw, int head_dim, int dtype, hipStream_t stream) {
+                  int wh, int ww, int st, int sh, int sw, int head_dim, int dtype, hipStream_t stream,
+                  bool no_alloc = false) {
   if (!q || !k || !v || !out) return BASA_ERR_NULL;
   if (n_mem < 0) return BASA_ERR_SHAPE;
   if (n_mem > 0 && (!kmem || !vmem)) return BASA_ERR_NULL;
@@ -104,8 +105,9 @@ int run_attention(const void* q, const void* k, const void* v, const int32_t* ro
   p.n_tokens = int32_t(N);
   p.route = route;
   const hipError_t e =
-      basa::launch_window_attention(q, k, v, out, p, head_dim, dtype == BASA_DTYPE_BF16, stream);
+      basa::launch_window_attention(q, k, v, out, p, head_dim, dtype == BASA_DTYPE_BF16, no_alloc, stream);
   if (e == hipErrorInvalidConfiguration) return BASA_ERR_OVERFLOW;
+  if (no_alloc && e == hipErrorOutOfMemory) return BASA_ERR_SCRATCH;
   return e == hipSuccess ? BASA_OK : BASA_ERR_HIP;
 }
 
@@ -118,6 +120,13 @@ int basa_window_attn_fwd(const void* q, const void* k, const void* v, void* out,
                          hipStream_t stream) {
   return run_attention(q, k, v, nullptr, nullptr, nullptr, 0, out, nullptr, B, heads, T, H, W, wt, wh, ww, st, sh,
                        sw, head_dim, dtype, stream);
+}
+
+int basa_window_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, int B, int heads, int T,
+                                 int H, int W, int wt, int wh, int ww, int st, int sh, int sw, int head_dim,
+                                 int dtype, hipStream_t stream) {
+  return run_attention(q, k, v, nullptr, nullptr, nullptr, 0, out, nullptr, B, heads, T, H, W, wt, wh, ww, st, sh,
+                       sw, head_dim, dtype, stream, true);
 }
 
 int basa_full_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int heads, int N,
@@ -235,11 +244,12 @@ const char* basa_status_string(int status) {
     case BASA_ERR_OVERFLOW: return "size exceeds the 32-bit per-head indexing";
     case BASA_ERR_HIP: return "HIP launch error";
     case BASA_ERR_ALIGN: return "tensor pointer is not 16-byte aligned (perm: 4-byte)";
+    case BASA_ERR_SCRATCH: return "the call needs more than the static scratch buffer holds";
     default: return "unknown status";
   }
 }
 
-int basa_version(void) { return (1 << 16) | 3; }
+int basa_version(void) { return (1 << 16) | 4; }
 
 // Interleaved shift schedule, BASA §3.1: per axis the offsets (i * delta) mod w with
 // delta = max(1, floor(w / L)) are taken alternately from their first ceil(L/2) and the

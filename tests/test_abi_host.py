@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(8):
+    for code in range(9):
         s = _lib.status_string(code)
         assert s and s != "unknown status"
     assert _lib.status_string(99) == "unknown status"
@@ -76,6 +76,22 @@ def _win(q=A, k=Bp, v=Cp, out=D, B=1, heads=2, grid=(1, 16, 16), window=(1, 8, 8
 ])
 def test_argument_errors_return_codes(kw, code):
     assert _win(**kw) == code
+
+
+ERROR_CASES = [(dict(q=None), 1), (dict(window=(1, 6, 8)), 2), (dict(head_dim=96), 3), (dict(out=A), 4),
+               (dict(B=65536, heads=65536), 5), (dict(q=A + 8), 7)]
+
+
+@pytest.mark.parametrize("kw,code", ERROR_CASES)
+def test_noalloc_argument_errors_match(kw, code):
+    """The no-allocation entry point validates exactly like basa_window_attn_fwd."""
+    args = dict(q=A, k=Bp, v=Cp, out=D, B=1, heads=2, grid=(1, 16, 16), window=(1, 8, 8), shift=(0, 4, 4),
+                head_dim=64, dtype=0)
+    args.update(kw)
+    rc = _lib.load().basa_window_attn_fwd_noalloc(args["q"], args["k"], args["v"], args["out"], args["B"],
+                                                  args["heads"], *args["grid"], *args["window"], *args["shift"],
+                                                  args["head_dim"], args["dtype"], None)
+    assert rc == code == _win(**kw)
 
 
 def test_full_and_perm_argument_errors():
