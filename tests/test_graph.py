@@ -1,12 +1,14 @@
 """The entry points inside a captured HIP graph.
 
 A DiT's denoising loop calls the attention once per layer and step with the same shapes,
-which is what graph capture is for. The library's calls make no allocation, no memset
-and no synchronisation, so they can be captured. Each test captures a sequence of calls
-into a graph (`torch.cuda.graph`), then replays it several times with new inputs copied
-into the captured tensors, with eager work and a synchronisation between replays, and
-checks that every replay equals the eager result bit for bit (the kernels use no atomics,
-so a launch is deterministic).
+which is what graph capture is for. Inside a capture the library's calls make no
+allocation, no memset and no synchronisation: a call whose last round of work items is
+split (per-item kernel) uses the workspace its stream got from an earlier call outside the
+capture, and the no-allocation entry point uses the library's static array. Each test
+captures a sequence of calls into a graph (`torch.cuda.graph`), then replays it several
+times with new inputs copied into the captured tensors, with eager work and a
+synchronisation between replays, and checks that every replay equals the eager result bit
+for bit (a launch is deterministic: split items are merged in a fixed order).
 """
 import pytest
 import torch
@@ -96,3 +98,63 @@ def test_memory_path_graph_replays():
         assert torch.equal(kmem, rkm) and torch.equal(vmem, rvm), f"replay {r}: pooled memory differs"
         assert torch.equal(out, rout), f"replay {r}: output differs from eager"
         assert torch.equal(lse, rlse), f"replay {r}: log-sum-exp differs from eager"
+
+
+# 17-tile windows (per-item kernel), 19 heads: 380 work items, the last 124 split in two
+SPLIT_GRID, SPLIT_WINDOW, SPLIT_SHIFT = (1, 48, 90), (1, 24, 45), (0, 7, -11)
+
+
+def _replay_and_compare(graph, captured, outs, call, shape, seed0):
+    q, k, v = captured
+    for r in range(REPLAYS):
+        nq, nk, nv = _new_inputs(shape, torch.bfloat16, seed0 + r)
+        q.copy_(nq)
+        k.copy_(nk)
+        v.copy_(nv)
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = torch.empty_like(q)
+        call(nq, nk, nv, ref)  # eager, on fresh tensors
+        torch.cuda.synchronize()
+        assert torch.equal(outs, ref), f"replay {r}: graph output differs from eager"
+
+
+def test_split_items_graph_replays():
+    """Captured on a stream that made its split workspace in an eager call before."""
+    N = SPLIT_GRID[0] * SPLIT_GRID[1] * SPLIT_GRID[2]
+    shape = (1, 19, N, 128)
+    q, k, v = _new_inputs(shape, torch.bfloat16, 3)
+    out = torch.empty_like(q)
+    s = torch.cuda.Stream()
+    log_case("graph split items", shape, SPLIT_GRID, SPLIT_WINDOW, SPLIT_SHIFT)
+
+    def call(q_, k_, v_, o_):
+        with torch.cuda.stream(s):
+            _lib.window_attn_fwd(q_, k_, v_, o_, SPLIT_GRID, SPLIT_WINDOW, SPLIT_SHIFT, stream=s)
+
+    call(q, k, v, out)  # outside the capture: the stream's workspace is made here
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        _lib.window_attn_fwd(q, k, v, out, SPLIT_GRID, SPLIT_WINDOW, SPLIT_SHIFT, stream=s)
+    _replay_and_compare(graph, (q, k, v), out, call, shape, 300)
+
+
+def test_noalloc_graph_replays():
+    """The no-allocation entry point, captured on a stream it has never run on."""
+    N = SPLIT_GRID[0] * SPLIT_GRID[1] * SPLIT_GRID[2]
+    shape = (1, 19, N, 128)
+    q, k, v = _new_inputs(shape, torch.bfloat16, 4)
+    out = torch.empty_like(q)
+    log_case("graph no-alloc", shape, SPLIT_GRID, SPLIT_WINDOW, SPLIT_SHIFT)
+
+    def call(q_, k_, v_, o_):
+        _lib.window_attn_fwd_noalloc(q_, k_, v_, o_, SPLIT_GRID, SPLIT_WINDOW, SPLIT_SHIFT)
+
+    call(q, k, v, out)  # reads the CU count and the array's address, allocates nothing
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        _lib.window_attn_fwd_noalloc(q, k, v, out, SPLIT_GRID, SPLIT_WINDOW, SPLIT_SHIFT, stream=s)
+    _replay_and_compare(graph, (q, k, v), out, call, shape, 400)
