@@ -158,3 +158,30 @@ def test_noalloc_graph_replays():
     with torch.cuda.graph(graph, stream=s):
         _lib.window_attn_fwd_noalloc(q, k, v, out, SPLIT_GRID, SPLIT_WINDOW, SPLIT_SHIFT, stream=s)
     _replay_and_compare(graph, (q, k, v), out, call, shape, 400)
+
+
+def test_split_call_captured_on_a_new_stream_runs_unsplit():
+    """Captured on a stream with no workspace yet: the call cannot allocate inside the
+    capture, so it runs without the split. Its replays agree with each other bit for bit and
+    with the eager (split) result to the bf16 bar (a different summation order)."""
+    from gpu_util import assert_parity, to_host
+    N = SPLIT_GRID[0] * SPLIT_GRID[1] * SPLIT_GRID[2]
+    shape = (1, 19, N, 128)
+    q, k, v = _new_inputs(shape, torch.bfloat16, 5)
+    out = torch.empty_like(q)
+    log_case("graph, stream without workspace", shape, SPLIT_GRID, SPLIT_WINDOW, SPLIT_SHIFT)
+    ref = torch.empty_like(q)
+    _lib.window_attn_fwd(q, k, v, ref, SPLIT_GRID, SPLIT_WINDOW, SPLIT_SHIFT)  # eager, default stream
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        _lib.window_attn_fwd(q, k, v, out, SPLIT_GRID, SPLIT_WINDOW, SPLIT_SHIFT, stream=s)
+    first = None
+    for r in range(REPLAYS):
+        graph.replay()
+        torch.cuda.synchronize()
+        if first is None:
+            first = out.clone()
+        assert torch.equal(out, first), f"replay {r} differs from the first"
+    assert_parity(to_host(first), to_host(ref), "bf16", "graph without workspace vs eager")
