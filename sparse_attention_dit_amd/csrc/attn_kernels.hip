@@ -631,13 +631,16 @@ __device__ __forceinline__ void win_attn_bf16_item(const uint16_t* __restrict__ 
     const Bf16KernelArgs& a = kernel_args();
     const uint32_t pair = item - a.split_from;
     f32x4_t* part = reinterpret_cast<f32x4_t*>(a.part);
-    f32x4_t* mine = part + ((uint64_t(pair) * 2 + uint64_t(half)) * NW + uint64_t(wave)) * (SP::CHUNKS * 64) + lane;
-    const f32x4_t* other = part + ((uint64_t(pair) * 2 + uint64_t(half ^ 1)) * NW + uint64_t(wave)) * (SP::CHUNKS * 64) + lane;
+    const uint64_t wave_chunks = uint64_t(SP::CHUNKS) * 64;
+    f32x4_t* mine = part + ((uint64_t(pair) * 2 + uint64_t(half)) * NW + uint64_t(wave)) * wave_chunks + lane;
+    const f32x4_t* other =
+        part + ((uint64_t(pair) * 2 + uint64_t(half ^ 1)) * NW + uint64_t(wave)) * wave_chunks + lane;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        mine[(db * 4 + j) * 64] = f32x4_t{oacc[db][4 * j], oacc[db][4 * j + 1], oacc[db][4 * j + 2], oacc[db][4 * j + 3]};
+        mine[(db * 4 + j) * 64] =
+            f32x4_t{oacc[db][4 * j], oacc[db][4 * j + 1], oacc[db][4 * j + 2], oacc[db][4 * j + 3]};
     mine[DB * 4 * 64] = f32x4_t{m_run, l_run, 0.0f, 0.0f};
     __shared__ uint32_t first;
     __syncthreads();
@@ -1463,6 +1466,12 @@ static hipError_t launch_bf16(const void* q, const void* k, const void* v, void*
   uint32_t slots = 0;
   const hipError_t e = persistent_slots(&slots);
   if (e != hipSuccess) return e;
+  // the static array's address on this device, taken on the first no_alloc call there
+  void* scratch_ptr = nullptr;
+  if (no_alloc) {
+    const hipError_t es = scratch_address(&scratch_ptr);
+    if (es != hipSuccess) return es;
+  }
   const uint32_t grid = blocks < slots ? uint32_t(blocks) : slots;
   // The stream kernel takes the item transitions off the critical path (measured: FLUX-1024,
   // 4 tiles, 8 % faster than the per-item kernel; FLUX-2048 and FLUX-4096, 16 tiles, 2-4 %
@@ -1485,8 +1494,7 @@ static hipError_t launch_bf16(const void* q, const void* k, const void* v, void*
     uint64_t counters = 0;
     if (no_alloc) {
       if (tail > kScratchSlots / 2) return hipErrorOutOfMemory;
-      const hipError_t es = scratch_address(&ws);
-      if (es != hipSuccess) return es;
+      ws = scratch_ptr;
       counters = split_counter_offset(kScratchSlots);
       // the array keeps the last call's contents: the counters of this call start at zero
       hipLaunchKernelGGL(clear_counters_kernel, dim3((tail + 255) / 256), dim3(256), 0, stream,
