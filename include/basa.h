@@ -28,8 +28,9 @@
  *     (device, stream): for 256 compute units 35.7 MB (128 items x 2 halves x 139,264
  *     bytes, and 4 bytes per item), allocated with hipMalloc, its counters cleared with
  *     hipMemsetAsync on `stream`, on the first call on that stream that splits, and kept
- *     until the process ends. Calls on one stream share it (they run in order); calls on
- *     different streams never do. A stream destroyed while such a call on it still runs
+ *     until the process ends; at most 16 per device (calls on further streams run
+ *     unsplit). Calls on one stream share it (they run in order); calls on different
+ *     streams never do. A stream destroyed while such a call on it still runs
  *     must not be followed, before that call ends, by a new stream with the same handle.
  *     If the allocation fails, or the stream is being captured into a graph and has no
  *     workspace yet, the call runs unsplit (the same result within the bf16 bounds).

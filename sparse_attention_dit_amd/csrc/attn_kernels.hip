@@ -1409,19 +1409,23 @@ __global__ __launch_bounds__(256) void clear_counters_kernel(uint32_t* c, uint32
 }
 
 // The library's own workspace, one per (device, stream), made on the first launch on that
-// stream that splits items and kept until the process ends. Launches on one stream run in
-// order, so they can share it; launches on different streams never do. Returns null (no
-// split) while the stream is being captured into a graph and has no workspace yet, or when
-// the allocation fails.
+// stream that splits items and kept until the process ends; at most kMaxWorkspaces per
+// device. Launches on one stream run in order, so they can share it; launches on different
+// streams never do. Returns null (no split) while the stream is being captured into a graph
+// and has no workspace yet, when the device already has kMaxWorkspaces, or when the
+// allocation fails.
+constexpr int kMaxWorkspaces = 16;
 static void* split_workspace(hipStream_t stream, uint32_t slots) {
   static std::mutex mu;
   static std::map<std::pair<int, hipStream_t>, void*> made;
+  static std::map<int, int> per_device;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return nullptr;
   std::lock_guard<std::mutex> lock(mu);
   const auto key = std::make_pair(dev, stream);
   const auto it = made.find(key);
   if (it != made.end()) return it->second;
+  if (per_device[dev] >= kMaxWorkspaces) return nullptr;
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return nullptr;
   void* ws = nullptr;
@@ -1436,6 +1440,7 @@ static void* split_workspace(hipStream_t stream, uint32_t slots) {
     return nullptr;
   }
   made.emplace(key, ws);
+  ++per_device[dev];
   return ws;
 }
 
