@@ -58,12 +58,15 @@ EDGE = [
 ]
 
 
-# per-item kernel (windows of more than 16 key tiles), 256 < items <= 384: the last round is
-# split. Ragged 17-tile windows (1080 keys), so the halves are 9 and 8 tiles and the second
-# half ends in a partial tile. name, heads, head_dim, grid, window, shift, seed
+# per-item kernel (windows of more than 16 or fewer than 3 key tiles), 256 < items <= 384:
+# the last round is split. Ragged 17-tile windows (1080 keys), so the halves are 9 and 8
+# tiles and the second half ends in a partial tile; and 2-tile windows with a last round of
+# exactly half the grid (384 items: 256 halves of one tile each).
+# name, heads, head_dim, grid, window, shift, seed
 SPLIT = [
     ("split-d128-w1080", 19, 128, (1, 48, 90), (1, 24, 45), (0, 7, -11), 321),
     ("split-d64-w1080", 18, 64, (1, 48, 90), (1, 24, 45), (0, -5, 13), 322),
+    ("split-d128-w128-half-grid", 48, 128, (1, 32, 32), (1, 8, 16), (0, 3, 5), 323),
 ]
 
 
@@ -71,7 +74,8 @@ def test_split_cases_have_a_short_last_round():
     for name, heads, d, grid, window, *_ in SPLIT:
         n = work_items(1, heads, grid, window)
         assert CUS < n <= CUS + CUS // 2, (name, n)
-        assert math.ceil(int(np.prod(window)) / 64) > 16, name
+        tiles = math.ceil(int(np.prod(window)) / 64)
+        assert tiles > 16 or 2 <= tiles < 3, name
 
 
 @pytest.mark.gpu
